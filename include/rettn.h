@@ -1,0 +1,181 @@
+/*
+ * rettn.h -- C ABI of the Re-ttention sparse-attention library for MI355X (gfx950).
+ *
+ * What it computes.  The Re-ttention project page ("Re-ttention: Ultra Sparse
+ * Visual Generation via Attention Statistical Reshape") describes attention for
+ * diffusion transformers that keeps only a small subset of the keys (Abstract:
+ * as few as 3.1% of the tokens) and corrects the resulting softmax
+ * normalisation shift with statistics cached at an earlier denoising step
+ * (teaser paragraph), namely the ratio of sparse to full softmax denominators
+ * and the residual contribution of the masked-out tokens (core-mechanism
+ * paragraph under the Abstract).  The library fixes that description as follows,
+ * per batch b, head h, query row t (alpha = 1/sqrt(d), blocks of 64 tokens):
+ *
+ *   rt_select_blocks        Qb_i, Kb_j = mean of the rows of block i (j); pooled
+ *                           logits S_ij = alpha <Qb_i, Kb_j> (float32);
+ *                           kept list I_i = forced blocks plus the best
+ *                           (keep - n_forced) other blocks by (S_ij descending,
+ *                           j ascending), stored ascending.
+ *   rt_calibrate            dense attention over all keys that also records
+ *                           m = max_j s_j, Z_full = sum_j e^{s_j - m},
+ *                           Z_sparse = sum over keys of kept blocks of e^{s_j - m},
+ *                           R = sum over keys of masked blocks of e^{s_j - m} v_j,
+ *                           and the kept list, into the statistics cache.
+ *   rt_sparse_attn_reshape  attention over the kept blocks only (m, Z, N) and
+ *                           O = (N e^{m-M} + R_c e^{m_c-M}) / (Z e^{m-M} Z_full_c / Z_sparse_c),
+ *                           M = max(m, m_c), with the cached (m_c, Z_full_c,
+ *                           Z_sparse_c, R_c) of the same layer.
+ *   rt_attention_step       the denoising schedule: select + calibrate on steps
+ *                           where step % period == 0 (period <= 0: step 0 only),
+ *                           the sparse reshape on all other steps.
+ *
+ * Conventions for every call.
+ *  - Tensors are row-major and contiguous: q, k, v, o are [B, H, N, d_pad]
+ *    (bf16 or float32 per rt_shape.dtype); channels d..d_pad-1 of q, k, v must
+ *    be zero and are written as zero in o.  Device pointers must be 16-byte
+ *    aligned.
+ *  - All device work is enqueued asynchronously on `stream` (a hipStream_t;
+ *    NULL = the null stream).  The library never allocates or frees device
+ *    memory, never synchronises the device, and keeps no device state other
+ *    than what the caller's buffers hold.
+ *  - The caller owns every device buffer (inputs, outputs, workspace, cache
+ *    memory).  The library owns only the small host handle rt_stats_cache.
+ *  - Validation happens first: a call that returns an error has enqueued
+ *    nothing and touched no device memory.  A failed kernel launch returns
+ *    RT_E_LAUNCH.  Faults during execution surface at the caller's next
+ *    synchronisation.  rt_last_error() gives a thread-local description of
+ *    the last failure.
+ *  - Empty problems (B, H or N equal to 0) are valid and enqueue nothing;
+ *    their pointers may be NULL.
+ *  - Limits: block == 64, d_pad in {64, 80}, 1 <= d <= d_pad,
+ *    1 <= keep <= Nb = ceil(N/64), N <= 65536, 0 <= n_forced <= keep.
+ *  - Calls on the same cache layer must not overlap in time from several
+ *    host threads; calls on different layers may.
+ */
+#ifndef RETTN_H
+#define RETTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RT_OK = 0,
+  RT_E_ARG = 1,        /* null pointer, misaligned pointer, bad enum value */
+  RT_E_SHAPE = 2,      /* shape outside the limits above */
+  RT_E_DTYPE = 3,      /* dtype not supported for this call */
+  RT_E_STATE = 4,      /* layer not calibrated, or cache shape mismatch */
+  RT_E_WORKSPACE = 5,  /* workspace or cache memory too small */
+  RT_E_LAUNCH = 6,     /* the HIP runtime rejected a kernel launch */
+  RT_E_DEVICE = 7      /* no usable gfx950 device for the current HIP device */
+} rt_status;
+
+typedef enum { RT_BF16 = 0, RT_F32 = 1 } rt_dtype;
+
+typedef struct {
+  int32_t B, H, N;   /* batch, heads, tokens */
+  int32_t d;         /* true head dim: softmax scale 1/sqrt(d) */
+  int32_t d_pad;     /* stored head dim (row length of q, k, v, o, R) */
+  int32_t block;     /* tokens per block; must be 64 */
+  int32_t keep;      /* kept key blocks per query block, forced ones included */
+  int32_t dtype;     /* rt_dtype of q, k, v, o */
+} rt_shape;
+
+/* Opaque host handle over caller-owned device memory. */
+typedef struct rt_stats_cache rt_stats_cache;
+
+/* Device pointers of one layer of the statistics cache.
+ *   m, z_full, z_sparse : float32 [B, H, N]
+ *   R                   : float32 [B, H, N, d_pad], row-major
+ *   idx                 : int32   [B, H, Nb, keep], each row ascending
+ * `valid` is 1 once the layer has been calibrated (or marked valid).       */
+typedef struct {
+  float* m;
+  float* z_full;
+  float* z_sparse;
+  float* R;
+  int32_t* idx;
+  int64_t rows;      /* B*H*N */
+  int32_t valid;
+} rt_stats_view;
+
+const char* rt_status_string(int32_t status);
+const char* rt_last_error(void);
+int32_t rt_version(void);
+
+/* Number of key blocks ceil(N / 64), or -1 for an invalid shape. */
+int32_t rt_num_blocks(const rt_shape* shape);
+
+/* ---- block selector (project page, Abstract: attention over a subset of tokens) ----
+ * Workspace: float32 pooled means of q and k, 2 * B*H*Nb*d_pad*4 bytes (+ alignment).
+ * q, k      : device [B,H,N,d_pad].
+ * forced    : HOST array of n_forced distinct block indices in [0, Nb), or NULL.
+ *             They are always kept and count toward `keep`.
+ * block_idx : device int32 [B,H,Nb,keep] output, each row ascending.
+ * pooled_scores : device float32 [B,H,Nb,Nb] output of S_ij, or NULL.      */
+size_t rt_select_workspace_bytes(const rt_shape* shape);
+rt_status rt_select_blocks(const rt_shape* shape, const void* q, const void* k,
+                           const int32_t* forced, int32_t n_forced,
+                           int32_t* block_idx, float* pooled_scores,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- statistics cache (teaser paragraph: statistics cached across denoising steps) ----
+ * rt_stats_cache_bytes : device bytes for n_layers layers of `shape`.
+ * rt_stats_cache_init  : wraps caller-owned device memory `dev_mem` of `bytes`;
+ *                        every layer starts invalid.  *out receives a host handle.
+ * rt_stats_cache_view  : device pointers of one layer (for inspection, save and
+ *                        restore; the memory is the caller's).
+ * rt_stats_cache_set_valid : marks a layer valid (1) or invalid (0), e.g. after
+ *                        restoring its contents through the view.
+ * rt_stats_cache_invalidate : marks one layer, or all layers (layer = -1), invalid.
+ * rt_stats_cache_destroy : frees the host handle only; never touches device memory. */
+size_t rt_stats_cache_bytes(const rt_shape* shape, int32_t n_layers);
+rt_status rt_stats_cache_init(rt_stats_cache** out, const rt_shape* shape, int32_t n_layers,
+                              void* dev_mem, size_t bytes);
+rt_status rt_stats_cache_view(const rt_stats_cache* cache, int32_t layer, rt_stats_view* out);
+rt_status rt_stats_cache_set_valid(rt_stats_cache* cache, int32_t layer, int32_t valid);
+rt_status rt_stats_cache_invalidate(rt_stats_cache* cache, int32_t layer);
+rt_status rt_stats_cache_destroy(rt_stats_cache* cache);
+
+/* ---- calibration step (core-mechanism paragraph: record the sparse/full denominator
+ * ratio and the masked tokens' residual) ----
+ * block_idx : device int32 [B,H,Nb,keep] kept lists (from rt_select_blocks); copied
+ *             into the cache, so the caller may reuse the buffer afterwards.
+ * o         : device [B,H,N,d_pad] output = dense softmax attention.
+ * The cache shape must equal `shape`.  Marks `layer` valid.                 */
+rt_status rt_calibrate(const rt_shape* shape, const void* q, const void* k, const void* v,
+                       const int32_t* block_idx, rt_stats_cache* cache, int32_t layer,
+                       void* o, void* stream);
+
+/* ---- sparse step with statistical reshape (teaser and core-mechanism paragraphs) ----
+ * block_idx : device kept lists, or NULL to use the lists cached at calibration
+ *             (the reading this library takes: the masked set stays that of the
+ *             calibration step until the next calibration).
+ * Returns RT_E_STATE if `layer` is not valid.                               */
+rt_status rt_sparse_attn_reshape(const rt_shape* shape, const void* q, const void* k,
+                                 const void* v, const int32_t* block_idx,
+                                 const rt_stats_cache* cache, int32_t layer, void* o,
+                                 void* stream);
+
+/* ---- denoising schedule (teaser paragraph: statistics reused across steps) ----
+ * 1 if `step` is a calibration step for `period` (period <= 0: only step 0).   */
+int32_t rt_schedule_is_calibration(int32_t step, int32_t period);
+
+/* One attention call of a denoising schedule for one layer: on a calibration
+ * step, rt_select_blocks (into the workspace) then rt_calibrate; otherwise
+ * rt_sparse_attn_reshape with the cached lists.  Workspace bytes:
+ * rt_step_workspace_bytes.  *did_calibrate (may be NULL) receives 1 or 0.   */
+size_t rt_step_workspace_bytes(const rt_shape* shape);
+rt_status rt_attention_step(const rt_shape* shape, const void* q, const void* k, const void* v,
+                            const int32_t* forced, int32_t n_forced, rt_stats_cache* cache,
+                            int32_t layer, int32_t step, int32_t period, void* o,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            int32_t* did_calibrate);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RETTN_H */

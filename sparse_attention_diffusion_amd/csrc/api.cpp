@@ -1,0 +1,382 @@
+// C-ABI host layer: argument validation, statistics-cache layout, schedule,
+// and kernel launches on the caller's stream.  No device allocation, no
+// device synchronisation (unless RETTN_DEBUG_SYNC=1 is set in the environment).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/rettn.h"
+#include "internal.h"
+
+using rettn::AttnArgs;
+using rettn::AttnMode;
+using rettn::SelectArgs;
+
+struct rt_stats_cache {
+  rt_shape shape;
+  int32_t n_layers;
+  char* base;
+  size_t bytes;
+  size_t off_m, off_zf, off_zs, off_R, off_idx, layer_stride;
+  std::vector<int32_t> valid;
+};
+
+namespace {
+
+constexpr int32_t kVersion = 1;
+constexpr size_t kAlign = 256;
+
+thread_local std::string g_error;
+
+rt_status fail(rt_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t nblocks(int32_t N) { return (N + 63) / 64; }
+
+bool is_empty(const rt_shape* s) { return s->B == 0 || s->H == 0 || s->N == 0; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_bytes(const rt_shape* s) { return s->dtype == RT_BF16 ? 2 : 4; }
+
+rt_status check_shape(const rt_shape* s) {
+  if (s == nullptr) return fail(RT_E_ARG, "shape is NULL");
+  if (s->dtype != RT_BF16 && s->dtype != RT_F32) return fail(RT_E_DTYPE, "dtype %d is not RT_BF16 or RT_F32", s->dtype);
+  if (s->B < 0 || s->H < 0 || s->N < 0) return fail(RT_E_SHAPE, "negative B/H/N (%d, %d, %d)", s->B, s->H, s->N);
+  if (s->block != 64) return fail(RT_E_SHAPE, "block must be 64 (got %d)", s->block);
+  if (s->d_pad != 64 && s->d_pad != 80) return fail(RT_E_SHAPE, "d_pad must be 64 or 80 (got %d)", s->d_pad);
+  if (s->d < 1 || s->d > s->d_pad) return fail(RT_E_SHAPE, "need 1 <= d <= d_pad (d=%d, d_pad=%d)", s->d, s->d_pad);
+  if (s->N > 65536) return fail(RT_E_SHAPE, "N=%d exceeds 65536", s->N);
+  if (is_empty(s)) return RT_OK;
+  const int64_t nb = nblocks(s->N);
+  if (s->keep < 1 || s->keep > nb) return fail(RT_E_SHAPE, "need 1 <= keep <= Nb (keep=%d, Nb=%lld)", s->keep, (long long)nb);
+  if ((int64_t)s->B * s->H * nb > 0x7fffffffLL / 8) return fail(RT_E_SHAPE, "B*H*Nb too large");
+  return RT_OK;
+}
+
+bool same_shape(const rt_shape& a, const rt_shape& b) {
+  return a.B == b.B && a.H == b.H && a.N == b.N && a.d == b.d && a.d_pad == b.d_pad && a.block == b.block &&
+         a.keep == b.keep && a.dtype == b.dtype;
+}
+
+// Current device must be a gfx950; answered once per device.
+rt_status check_device() {
+  static std::mutex mu;
+  static std::vector<int> known;  // -1 unknown, 0 bad, 1 good
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RT_E_DEVICE, "no HIP device: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)known.size() <= dev) known.resize(dev + 1, -1);
+  if (known[dev] < 0) {
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess) return fail(RT_E_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    known[dev] = std::strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+    if (!known[dev]) return fail(RT_E_DEVICE, "device %d is %s, this library is built for gfx950", dev, p.gcnArchName);
+  }
+  return known[dev] ? RT_OK : fail(RT_E_DEVICE, "device %d is not a gfx950", dev);
+}
+
+bool debug_sync() {
+  static int v = [] {
+    const char* e = std::getenv("RETTN_DEBUG_SYNC");
+    return e != nullptr && e[0] == '1';
+  }();
+  return v != 0;
+}
+
+rt_status launched(hipError_t e, hipStream_t s, const char* what) {
+  if (e != hipSuccess) return fail(RT_E_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+  if (debug_sync()) {
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(RT_E_LAUNCH, "%s failed at sync: %s", what, hipGetErrorString(e));
+  }
+  return RT_OK;
+}
+
+void layout(rt_stats_cache* c) {
+  const rt_shape& s = c->shape;
+  const size_t rows = (size_t)s.B * s.H * s.N;
+  const size_t lists = (size_t)s.B * s.H * nblocks(s.N) * s.keep;
+  size_t off = 0;
+  c->off_m = off; off += align_up(rows * 4);
+  c->off_zf = off; off += align_up(rows * 4);
+  c->off_zs = off; off += align_up(rows * 4);
+  c->off_R = off; off += align_up(rows * s.d_pad * 4);
+  c->off_idx = off; off += align_up(lists * 4);
+  c->layer_stride = off;
+}
+
+AttnArgs attn_args(const rt_shape* s, const void* q, const void* k, const void* v, void* o, const int32_t* idx,
+                   const rt_stats_cache* c, int32_t layer) {
+  AttnArgs a{};
+  char* base = c->base + (size_t)layer * c->layer_stride;
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.idx = idx;
+  a.idx_cache = (int32_t*)(base + c->off_idx);
+  a.m = (float*)(base + c->off_m);
+  a.z_full = (float*)(base + c->off_zf);
+  a.z_sparse = (float*)(base + c->off_zs);
+  a.R = (float*)(base + c->off_R);
+  a.BH = s->B * s->H;
+  a.N = s->N;
+  a.Nb = (int32_t)nblocks(s->N);
+  a.keep = s->keep;
+  a.alpha = (float)(1.0 / std::sqrt((double)s->d));
+  return a;
+}
+
+rt_status check_tensors(const void* const* ptrs, const char* const* names, int n) {
+  for (int i = 0; i < n; ++i) {
+    if (ptrs[i] == nullptr) return fail(RT_E_ARG, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(RT_E_ARG, "%s is not 16-byte aligned", names[i]);
+  }
+  return RT_OK;
+}
+
+rt_status check_cache(const rt_shape* s, const rt_stats_cache* c, int32_t layer) {
+  if (c == nullptr) return fail(RT_E_ARG, "cache is NULL");
+  if (layer < 0 || layer >= c->n_layers) return fail(RT_E_ARG, "layer %d out of range [0, %d)", layer, c->n_layers);
+  if (!same_shape(*s, c->shape)) return fail(RT_E_STATE, "cache was initialised for a different shape");
+  return RT_OK;
+}
+
+size_t select_ws(const rt_shape* s) {
+  const size_t pooled = (size_t)s->B * s->H * nblocks(s->N) * s->d_pad * 4;
+  return 2 * align_up(pooled);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rt_status_string(int32_t st) {
+  switch (st) {
+    case RT_OK: return "RT_OK";
+    case RT_E_ARG: return "RT_E_ARG: invalid argument";
+    case RT_E_SHAPE: return "RT_E_SHAPE: shape outside the supported limits";
+    case RT_E_DTYPE: return "RT_E_DTYPE: unsupported dtype";
+    case RT_E_STATE: return "RT_E_STATE: cache layer not calibrated or shape mismatch";
+    case RT_E_WORKSPACE: return "RT_E_WORKSPACE: workspace or cache memory too small";
+    case RT_E_LAUNCH: return "RT_E_LAUNCH: kernel launch failed";
+    case RT_E_DEVICE: return "RT_E_DEVICE: no usable gfx950 device";
+    default: return "unknown rt_status";
+  }
+}
+
+const char* rt_last_error(void) { return g_error.c_str(); }
+
+int32_t rt_version(void) { return kVersion; }
+
+int32_t rt_num_blocks(const rt_shape* s) {
+  if (s == nullptr || s->N < 0) return -1;
+  return (int32_t)nblocks(s->N);
+}
+
+size_t rt_select_workspace_bytes(const rt_shape* s) {
+  if (check_shape(s) != RT_OK) return 0;
+  return select_ws(s);
+}
+
+rt_status rt_select_blocks(const rt_shape* s, const void* q, const void* k, const int32_t* forced,
+                           int32_t n_forced, int32_t* block_idx, float* pooled_scores, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  rt_status st = check_shape(s);
+  if (st != RT_OK) return st;
+  if (is_empty(s)) return RT_OK;
+  const void* ptrs[] = {q, k, block_idx, workspace};
+  const char* names[] = {"q", "k", "block_idx", "workspace"};
+  if ((st = check_tensors(ptrs, names, 4)) != RT_OK) return st;
+  if (pooled_scores != nullptr && (reinterpret_cast<uintptr_t>(pooled_scores) & 3u))
+    return fail(RT_E_ARG, "pooled_scores is not 4-byte aligned");
+  if (ws_bytes < select_ws(s)) return fail(RT_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, select_ws(s));
+  const int32_t nb = (int32_t)nblocks(s->N);
+  if (n_forced < 0 || n_forced > s->keep) return fail(RT_E_ARG, "need 0 <= n_forced <= keep (n_forced=%d)", n_forced);
+  if (n_forced > 0 && forced == nullptr) return fail(RT_E_ARG, "forced is NULL with n_forced=%d", n_forced);
+  SelectArgs a{};
+  for (int32_t i = 0; i < n_forced; ++i) {
+    const int32_t j = forced[i];
+    if (j < 0 || j >= nb) return fail(RT_E_ARG, "forced[%d]=%d outside [0, %d)", i, j, nb);
+    if ((a.forced[j >> 5] >> (j & 31)) & 1u) return fail(RT_E_ARG, "forced block %d listed twice", j);
+    a.forced[j >> 5] |= 1u << (j & 31);
+  }
+  if ((st = check_device()) != RT_OK) return st;
+  const size_t pooled = align_up((size_t)s->B * s->H * nb * s->d_pad * 4);
+  a.q = q;
+  a.k = k;
+  a.qb = (float*)workspace;
+  a.kb = (float*)((char*)workspace + pooled);
+  a.idx = block_idx;
+  a.scores = pooled_scores;
+  a.BH = s->B * s->H;
+  a.N = s->N;
+  a.Nb = nb;
+  a.keep = s->keep;
+  a.alpha = (float)(1.0 / std::sqrt((double)s->d));
+  hipStream_t hs = (hipStream_t)stream;
+  return launched(rettn::launch_select(s->dtype == RT_BF16, s->d_pad, a, hs), hs, "rt_select_blocks");
+}
+
+size_t rt_stats_cache_bytes(const rt_shape* s, int32_t n_layers) {
+  if (check_shape(s) != RT_OK || n_layers < 1) return 0;
+  rt_stats_cache c{};
+  c.shape = *s;
+  layout(&c);
+  return c.layer_stride * (size_t)n_layers;
+}
+
+rt_status rt_stats_cache_init(rt_stats_cache** out, const rt_shape* s, int32_t n_layers, void* dev_mem,
+                              size_t bytes) {
+  if (out == nullptr) return fail(RT_E_ARG, "out is NULL");
+  *out = nullptr;
+  rt_status st = check_shape(s);
+  if (st != RT_OK) return st;
+  if (n_layers < 1) return fail(RT_E_ARG, "n_layers must be >= 1 (got %d)", n_layers);
+  const size_t need = rt_stats_cache_bytes(s, n_layers);
+  if (need > 0 && dev_mem == nullptr && !is_empty(s)) return fail(RT_E_ARG, "dev_mem is NULL");
+  if (dev_mem != nullptr && (reinterpret_cast<uintptr_t>(dev_mem) % kAlign) != 0)
+    return fail(RT_E_ARG, "dev_mem must be %zu-byte aligned", kAlign);
+  if (bytes < need) return fail(RT_E_WORKSPACE, "cache memory %zu < %zu bytes", bytes, need);
+  rt_stats_cache* c = new (std::nothrow) rt_stats_cache();
+  if (c == nullptr) return fail(RT_E_ARG, "host allocation failed");
+  c->shape = *s;
+  c->n_layers = n_layers;
+  c->base = (char*)dev_mem;
+  c->bytes = bytes;
+  layout(c);
+  c->valid.assign(n_layers, 0);
+  *out = c;
+  return RT_OK;
+}
+
+rt_status rt_stats_cache_view(const rt_stats_cache* c, int32_t layer, rt_stats_view* out) {
+  if (c == nullptr || out == nullptr) return fail(RT_E_ARG, "cache or out is NULL");
+  if (layer < 0 || layer >= c->n_layers) return fail(RT_E_ARG, "layer %d out of range [0, %d)", layer, c->n_layers);
+  char* base = c->base + (size_t)layer * c->layer_stride;
+  out->m = (float*)(base + c->off_m);
+  out->z_full = (float*)(base + c->off_zf);
+  out->z_sparse = (float*)(base + c->off_zs);
+  out->R = (float*)(base + c->off_R);
+  out->idx = (int32_t*)(base + c->off_idx);
+  out->rows = (int64_t)c->shape.B * c->shape.H * c->shape.N;
+  out->valid = c->valid[layer];
+  return RT_OK;
+}
+
+rt_status rt_stats_cache_set_valid(rt_stats_cache* c, int32_t layer, int32_t valid) {
+  if (c == nullptr) return fail(RT_E_ARG, "cache is NULL");
+  if (layer < 0 || layer >= c->n_layers) return fail(RT_E_ARG, "layer %d out of range [0, %d)", layer, c->n_layers);
+  c->valid[layer] = valid ? 1 : 0;
+  return RT_OK;
+}
+
+rt_status rt_stats_cache_invalidate(rt_stats_cache* c, int32_t layer) {
+  if (c == nullptr) return fail(RT_E_ARG, "cache is NULL");
+  if (layer == -1) {
+    for (auto& v : c->valid) v = 0;
+    return RT_OK;
+  }
+  if (layer < 0 || layer >= c->n_layers) return fail(RT_E_ARG, "layer %d out of range [0, %d)", layer, c->n_layers);
+  c->valid[layer] = 0;
+  return RT_OK;
+}
+
+rt_status rt_stats_cache_destroy(rt_stats_cache* c) {
+  delete c;
+  return RT_OK;
+}
+
+rt_status rt_calibrate(const rt_shape* s, const void* q, const void* k, const void* v, const int32_t* block_idx,
+                       rt_stats_cache* c, int32_t layer, void* o, void* stream) {
+  rt_status st = check_shape(s);
+  if (st != RT_OK) return st;
+  if ((st = check_cache(s, c, layer)) != RT_OK) return st;
+  if (is_empty(s)) {
+    c->valid[layer] = 1;
+    return RT_OK;
+  }
+  const void* ptrs[] = {q, k, v, block_idx, o};
+  const char* names[] = {"q", "k", "v", "block_idx", "o"};
+  if ((st = check_tensors(ptrs, names, 5)) != RT_OK) return st;
+  if ((st = check_device()) != RT_OK) return st;
+  AttnArgs a = attn_args(s, q, k, v, o, block_idx, c, layer);
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = s->dtype == RT_BF16 ? rettn::launch_attn_bf16(AttnMode::kCalibrate, s->d_pad, a, hs)
+                                     : rettn::launch_attn_f32(AttnMode::kCalibrate, s->d_pad, a, hs);
+  if ((st = launched(e, hs, "rt_calibrate")) != RT_OK) return st;
+  c->valid[layer] = 1;
+  return RT_OK;
+}
+
+rt_status rt_sparse_attn_reshape(const rt_shape* s, const void* q, const void* k, const void* v,
+                                 const int32_t* block_idx, const rt_stats_cache* c, int32_t layer, void* o,
+                                 void* stream) {
+  rt_status st = check_shape(s);
+  if (st != RT_OK) return st;
+  if ((st = check_cache(s, c, layer)) != RT_OK) return st;
+  if (!c->valid[layer]) return fail(RT_E_STATE, "layer %d has no valid statistics (calibrate first)", layer);
+  if (is_empty(s)) return RT_OK;
+  const void* ptrs[] = {q, k, v, o};
+  const char* names[] = {"q", "k", "v", "o"};
+  if ((st = check_tensors(ptrs, names, 4)) != RT_OK) return st;
+  if (block_idx != nullptr && !aligned16(block_idx)) return fail(RT_E_ARG, "block_idx is not 16-byte aligned");
+  if ((st = check_device()) != RT_OK) return st;
+  AttnArgs a = attn_args(s, q, k, v, o, nullptr, c, layer);
+  a.idx = block_idx != nullptr ? block_idx : a.idx_cache;
+  a.idx_cache = nullptr;
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = s->dtype == RT_BF16 ? rettn::launch_attn_bf16(AttnMode::kSparse, s->d_pad, a, hs)
+                                     : rettn::launch_attn_f32(AttnMode::kSparse, s->d_pad, a, hs);
+  return launched(e, hs, "rt_sparse_attn_reshape");
+}
+
+int32_t rt_schedule_is_calibration(int32_t step, int32_t period) {
+  if (step < 0) return 0;
+  if (period <= 0) return step == 0 ? 1 : 0;
+  return step % period == 0 ? 1 : 0;
+}
+
+size_t rt_step_workspace_bytes(const rt_shape* s) {
+  if (check_shape(s) != RT_OK) return 0;
+  const size_t lists = (size_t)s->B * s->H * nblocks(s->N) * s->keep * 4;
+  return select_ws(s) + align_up(lists);
+}
+
+rt_status rt_attention_step(const rt_shape* s, const void* q, const void* k, const void* v, const int32_t* forced,
+                            int32_t n_forced, rt_stats_cache* c, int32_t layer, int32_t step, int32_t period,
+                            void* o, void* workspace, size_t ws_bytes, void* stream, int32_t* did_calibrate) {
+  rt_status st = check_shape(s);
+  if (st != RT_OK) return st;
+  if ((st = check_cache(s, c, layer)) != RT_OK) return st;
+  if (step < 0) return fail(RT_E_ARG, "step must be >= 0 (got %d)", step);
+  const bool calib = rt_schedule_is_calibration(step, period) != 0;
+  if (did_calibrate != nullptr) *did_calibrate = calib ? 1 : 0;
+  if (!calib) return rt_sparse_attn_reshape(s, q, k, v, nullptr, c, layer, o, stream);
+  if (is_empty(s)) return rt_calibrate(s, q, k, v, nullptr, c, layer, o, stream);
+  if (workspace == nullptr) return fail(RT_E_ARG, "workspace is NULL");
+  if (ws_bytes < rt_step_workspace_bytes(s))
+    return fail(RT_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, rt_step_workspace_bytes(s));
+  int32_t* lists = (int32_t*)((char*)workspace + select_ws(s));
+  st = rt_select_blocks(s, q, k, forced, n_forced, lists, nullptr, workspace, select_ws(s), stream);
+  if (st != RT_OK) return st;
+  return rt_calibrate(s, q, k, v, lists, c, layer, o, stream);
+}
+
+}  // extern "C"

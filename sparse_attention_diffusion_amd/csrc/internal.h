@@ -1,0 +1,54 @@
+// Internal interface between the C-ABI host layer (api.cpp) and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rettn {
+
+constexpr int kBlock = 64;         // tokens per block
+constexpr int kMaxBlocks = 1024;   // Nb limit (N <= 65536)
+
+enum class AttnMode : int { kCalibrate = 0, kSparse = 1 };
+
+// Everything one attention launch needs.  Tensors are [BH, N, D] row-major.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const int32_t* idx;      // kept lists [BH, Nb, keep] used by this call
+  int32_t* idx_cache;      // calibrate: destination of the list copy (may be null)
+  float* m;                // statistics cache rows [BH, N]
+  float* z_full;
+  float* z_sparse;
+  float* R;                // [BH, N, D]
+  int32_t BH, N, Nb, keep;
+  float alpha;             // 1/sqrt(d)
+};
+
+struct SelectArgs {
+  const void* q;
+  const void* k;
+  float* qb;               // workspace [BH, Nb, D] float32
+  float* kb;
+  int32_t* idx;            // [BH, Nb, keep]
+  float* scores;           // [BH, Nb, Nb] or null
+  int32_t BH, N, Nb, keep;
+  float alpha;
+  uint32_t forced[kMaxBlocks / 32];  // bitmask of always-kept blocks
+};
+
+// Grid of `total` workgroups laid out so that each of the 8 XCDs (workgroups
+// are handed to XCDs round-robin by id) receives one contiguous range.
+struct XcdGrid {
+  uint32_t total, per;
+  __host__ __device__ uint32_t grid() const { return per * 8u; }
+  __device__ uint32_t linear(uint32_t wg) const { return (wg % 8u) * per + wg / 8u; }
+};
+inline XcdGrid make_xcd_grid(uint32_t total) { return XcdGrid{total, (total + 7u) / 8u}; }
+
+hipError_t launch_attn_bf16(AttnMode mode, int D, const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_f32(AttnMode mode, int D, const AttnArgs& a, hipStream_t s);
+hipError_t launch_select(bool bf16, int D, const SelectArgs& a, hipStream_t s);
+
+}  // namespace rettn

@@ -1,0 +1,94 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI
+and compare with the oracle.  The oracle never receives a value produced on the
+GPU; the GPU may receive oracle-made lists and statistics."""
+import numpy as np
+import torch
+
+import oracle
+from sparse_attention_diffusion_amd import configs, rettn, synth
+
+DEV = "cuda"
+# output tolerances: max |dO| <= 1e-2 max |O_ref|, L1-relative error <= 3e-3
+MAX_REL = 1e-2
+L1_REL = 3e-3
+
+
+def errors(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    diff = np.abs(got - ref)
+    return float(diff.max() / np.abs(ref).max()), float(diff.sum() / np.abs(ref).sum())
+
+
+def assert_close(got, ref, max_rel=MAX_REL, l1_rel=L1_REL, what="O"):
+    assert np.all(np.isfinite(np.asarray(got, dtype=np.float64))), f"{what}: non-finite values"
+    mx, l1 = errors(got, ref)
+    assert mx <= max_rel and l1 <= l1_rel, f"{what}: max-rel {mx:.3e} (<= {max_rel}), L1-rel {l1:.3e} (<= {l1_rel})"
+    return mx, l1
+
+
+def host(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def gpu_inputs(cfg, n_steps, seed=0):
+    """Stored (q, k, v) per step, generated on the GPU."""
+    return synth.steps(cfg, n_steps, seed=seed, device=DEV)
+
+
+def empty_out(sh):
+    return torch.zeros((sh.B, sh.H, sh.N, sh.d_pad), dtype=rettn.torch_dtype(sh), device=DEV)
+
+
+def select(sh, q, k, forced):
+    nb = rettn.num_blocks(sh)
+    idx = torch.full((sh.B, sh.H, nb, sh.keep), -1, dtype=torch.int32, device=DEV)
+    scores = torch.zeros((sh.B, sh.H, nb, nb), dtype=torch.float32, device=DEV)
+    ws = torch.empty(rettn.select_workspace_bytes(sh), dtype=torch.uint8, device=DEV)
+    rettn.rt_select_blocks(sh, q, k, forced, idx, scores, ws)
+    torch.cuda.synchronize()
+    return idx, scores
+
+
+def oracle_lists(cfg_like, q, k, forced, keep):
+    N, d = cfg_like["N"], cfg_like["d"]
+    return oracle.select_blocks(host(q), host(k), N, d, keep, forced)
+
+
+def valid_topk(scores_row, sel, keep, forced):
+    """The list is ascending, holds the forced blocks, and every other chosen
+    block beats every unchosen one by (score descending, index ascending)."""
+    sel = [int(x) for x in sel]
+    nb = len(scores_row)
+    if sel != sorted(set(sel)) or len(sel) != min(keep, nb) or not set(forced) <= set(sel):
+        return False
+    chosen = [j for j in sel if j not in forced]
+    other = [j for j in range(nb) if j not in sel]
+    if not chosen or not other:
+        return True
+    worst = min(chosen, key=lambda j: (scores_row[j], -j))
+    best = max(other, key=lambda j: (scores_row[j], -j))
+    return (scores_row[worst], -worst) > (scores_row[best], -best)
+
+
+def calibrate(sh, q, k, v, idx, cache, layer=0):
+    o = empty_out(sh)
+    rettn.rt_calibrate(sh, q, k, v, idx, cache, layer, o)
+    return o
+
+
+def sparse(sh, q, k, v, cache, layer=0, idx=None):
+    o = empty_out(sh)
+    rettn.rt_sparse_attn_reshape(sh, q, k, v, idx, cache, layer, o)
+    return o
+
+
+def block_rows(N, i):
+    return slice(i * 64, min(N, (i + 1) * 64))
+
+
+def sample_blocks(nb):
+    return sorted(set([0, min(3, nb - 1), min(4, nb - 1), nb // 2, nb - 1]))
+
+
+__all__ = ["configs", "synth", "rettn", "oracle"]

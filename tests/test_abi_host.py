@@ -1,0 +1,199 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no kernel launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from sparse_attention_diffusion_amd import rettn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "rettn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rt_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 17
+    lib = rettn.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(rettn.SYMBOLS) == names
+
+
+def test_version_and_strings():
+    assert rettn.lib().rt_version() == 1
+    for st in range(8):
+        assert rettn.lib().rt_status_string(st).decode().startswith("RT_")
+
+
+def test_num_blocks():
+    assert rettn.num_blocks(rettn.shape(1, 1, 17776, 64, 64, 9)) == 278
+    assert rettn.num_blocks(rettn.shape(1, 1, 64, 64, 64, 1)) == 1
+    assert rettn.num_blocks(rettn.shape(1, 1, 65, 64, 64, 1)) == 2
+    assert rettn.num_blocks(rettn.shape(1, 1, 0, 64, 64, 1)) == 0
+
+
+def test_schedule():
+    cal = [s for s in range(50) if rettn.schedule_is_calibration(s, 10)]
+    assert cal == [0, 10, 20, 30, 40]
+    assert [s for s in range(50) if rettn.schedule_is_calibration(s, 0)] == [0]
+    assert [s for s in range(50) if rettn.schedule_is_calibration(s, -1)] == [0]
+    assert not rettn.schedule_is_calibration(-3, 10)
+
+
+def cache_bytes_expected(B, H, N, D, keep, layers):
+    al = lambda x: (x + 255) // 256 * 256
+    rows = B * H * N
+    nb = (N + 63) // 64
+    per = 3 * al(rows * 4) + al(rows * D * 4) + al(B * H * nb * keep * 4)
+    return per * layers
+
+
+@pytest.mark.parametrize("B,H,N,D,keep,layers", [(2, 30, 17776, 64, 9, 1), (2, 48, 17776, 64, 9, 42),
+                                                  (2, 16, 1024, 80, 2, 1), (1, 2, 256, 64, 2, 3)])
+def test_cache_bytes(B, H, N, D, keep, layers):
+    sh = rettn.shape(B, H, N, 64 if D == 64 else 72, D, keep)
+    assert rettn.stats_cache_bytes(sh, layers) == cache_bytes_expected(B, H, N, D, keep, layers)
+
+
+def test_cogvideox5b_cache_size():
+    sh = rettn.shape(2, 48, 17776, 64, 64, 9)
+    gib = rettn.stats_cache_bytes(sh, 42) / 2**30
+    assert 17.5 < gib < 18.5  # about 19.3 GB
+
+
+def _fake_dev_memory(nbytes):
+    """Host bytes used as an opaque address: only pointer arithmetic happens on it."""
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8)
+    off = (-buf.data_ptr()) % 256
+    return buf, buf.data_ptr() + off
+
+
+def test_cache_layout_views():
+    sh = rettn.shape(1, 2, 100, 64, 64, 2, dtype="f32")
+    nbytes = rettn.stats_cache_bytes(sh, 3)
+    buf, addr = _fake_dev_memory(nbytes)
+    h = ctypes.c_void_p()
+    lib = rettn.lib()
+    assert lib.rt_stats_cache_init(ctypes.byref(h), ctypes.byref(sh), 3, ctypes.c_void_p(addr), nbytes) == 0
+    views = []
+    for layer in range(3):
+        v = rettn.RtStatsView()
+        assert lib.rt_stats_cache_view(h, layer, ctypes.byref(v)) == 0
+        assert v.valid == 0 and v.rows == 200
+        views.append(v)
+    ptrs = sorted(p for v in views for p in (v.m, v.z_full, v.z_sparse, v.R, v.idx))
+    assert ptrs[0] == addr and all(p % 256 == 0 for p in ptrs)
+    assert views[1].m - views[0].m == nbytes // 3
+    assert views[0].R - views[0].z_sparse >= 200 * 4
+    assert lib.rt_stats_cache_set_valid(h, 1, 1) == 0
+    v = rettn.RtStatsView()
+    lib.rt_stats_cache_view(h, 1, ctypes.byref(v))
+    assert v.valid == 1
+    assert lib.rt_stats_cache_invalidate(h, -1) == 0
+    lib.rt_stats_cache_view(h, 1, ctypes.byref(v))
+    assert v.valid == 0
+    assert lib.rt_stats_cache_view(h, 3, ctypes.byref(v)) == rettn.RT_E_ARG
+    assert lib.rt_stats_cache_destroy(h) == 0
+    del buf
+
+
+def test_cache_init_errors():
+    lib = rettn.lib()
+    sh = rettn.shape(1, 2, 100, 64, 64, 2)
+    nbytes = rettn.stats_cache_bytes(sh, 1)
+    buf, addr = _fake_dev_memory(nbytes)
+    h = ctypes.c_void_p()
+    assert lib.rt_stats_cache_init(ctypes.byref(h), ctypes.byref(sh), 1, ctypes.c_void_p(addr), nbytes - 1) \
+        == rettn.RT_E_WORKSPACE
+    assert lib.rt_stats_cache_init(ctypes.byref(h), ctypes.byref(sh), 0, ctypes.c_void_p(addr), nbytes) \
+        == rettn.RT_E_ARG
+    assert lib.rt_stats_cache_init(ctypes.byref(h), ctypes.byref(sh), 1, ctypes.c_void_p(addr + 16), nbytes) \
+        == rettn.RT_E_ARG
+    assert b"aligned" in lib.rt_last_error()
+    del buf
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("block", 32, rettn.RT_E_SHAPE), ("d_pad", 128, rettn.RT_E_SHAPE), ("d", 0, rettn.RT_E_SHAPE),
+    ("d", 65, rettn.RT_E_SHAPE), ("keep", 0, rettn.RT_E_SHAPE), ("keep", 3, rettn.RT_E_SHAPE),
+    ("dtype", 7, rettn.RT_E_DTYPE), ("N", 70000, rettn.RT_E_SHAPE), ("B", -1, rettn.RT_E_SHAPE),
+])
+def test_shape_validation(field, value, status):
+    sh = rettn.shape(1, 1, 100, 64, 64, 2)
+    setattr(sh, field, value)
+    lib = rettn.lib()
+    ws = ctypes.c_void_p(4096)
+    st = lib.rt_select_blocks(ctypes.byref(sh), ws, ws, None, 0, ws, None, ws, 1 << 30, None)
+    assert st == status, lib.rt_last_error()
+
+
+def test_select_argument_errors():
+    lib = rettn.lib()
+    sh = rettn.shape(1, 1, 200, 64, 64, 2)
+    p = ctypes.c_void_p(4096)
+    need = rettn.select_workspace_bytes(sh)
+    assert need == 2 * 4 * 64 * 4
+    assert lib.rt_select_blocks(ctypes.byref(sh), None, p, None, 0, p, None, p, need, None) == rettn.RT_E_ARG
+    assert lib.rt_select_blocks(ctypes.byref(sh), ctypes.c_void_p(4100), p, None, 0, p, None, p, need, None) \
+        == rettn.RT_E_ARG
+    assert lib.rt_select_blocks(ctypes.byref(sh), p, p, None, 0, p, None, p, need - 1, None) == rettn.RT_E_WORKSPACE
+    bad = (ctypes.c_int32 * 3)(0, 1, 2)
+    assert lib.rt_select_blocks(ctypes.byref(sh), p, p, bad, 3, p, None, p, need, None) == rettn.RT_E_ARG
+    dup = (ctypes.c_int32 * 2)(1, 1)
+    assert lib.rt_select_blocks(ctypes.byref(sh), p, p, dup, 2, p, None, p, need, None) == rettn.RT_E_ARG
+    oob = (ctypes.c_int32 * 1)(4)
+    assert lib.rt_select_blocks(ctypes.byref(sh), p, p, oob, 1, p, None, p, need, None) == rettn.RT_E_ARG
+
+
+def test_state_machine_without_gpu():
+    """Sparse before calibration is rejected on the host, before any device call."""
+    lib = rettn.lib()
+    sh = rettn.shape(1, 1, 128, 64, 64, 1)
+    nbytes = rettn.stats_cache_bytes(sh, 2)
+    buf, addr = _fake_dev_memory(nbytes)
+    h = ctypes.c_void_p()
+    assert lib.rt_stats_cache_init(ctypes.byref(h), ctypes.byref(sh), 2, ctypes.c_void_p(addr), nbytes) == 0
+    p = ctypes.c_void_p(4096)
+    assert lib.rt_sparse_attn_reshape(ctypes.byref(sh), p, p, p, None, h, 0, p, None) == rettn.RT_E_STATE
+    assert lib.rt_sparse_attn_reshape(ctypes.byref(sh), p, p, p, None, h, 2, p, None) == rettn.RT_E_ARG
+    other = rettn.shape(1, 1, 128, 64, 64, 2)
+    assert lib.rt_calibrate(ctypes.byref(other), p, p, p, p, h, 0, p, None) == rettn.RT_E_STATE
+    assert lib.rt_calibrate(ctypes.byref(sh), p, p, p, None, h, 0, p, None) == rettn.RT_E_ARG
+    did = ctypes.c_int32(-1)
+    st = lib.rt_attention_step(ctypes.byref(sh), p, p, p, None, 0, h, 0, 3, 10, p, p, 1 << 20, None,
+                               ctypes.byref(did))
+    assert st == rettn.RT_E_STATE and did.value == 0
+    lib.rt_stats_cache_destroy(h)
+    del buf
+
+
+def test_empty_problems_are_noops():
+    lib = rettn.lib()
+    for sh in (rettn.shape(0, 4, 100, 64, 64, 1), rettn.shape(2, 0, 100, 64, 64, 1), rettn.shape(2, 4, 0, 64, 64, 1)):
+        assert lib.rt_select_blocks(ctypes.byref(sh), None, None, None, 0, None, None, None, 0, None) == 0
+        h = ctypes.c_void_p()
+        nbytes = rettn.stats_cache_bytes(sh, 1)
+        buf, addr = _fake_dev_memory(nbytes)
+        assert lib.rt_stats_cache_init(ctypes.byref(h), ctypes.byref(sh), 1, ctypes.c_void_p(addr), nbytes) == 0
+        assert lib.rt_calibrate(ctypes.byref(sh), None, None, None, None, h, 0, None, None) == 0
+        assert lib.rt_sparse_attn_reshape(ctypes.byref(sh), None, None, None, None, h, 0, None, None) == 0
+        lib.rt_stats_cache_destroy(h)
+        del buf
+
+
+def test_no_device_is_reported_not_faked():
+    """Valid arguments without a gfx950 device give RT_E_DEVICE (no CPU fallback)."""
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    lib = rettn.lib()
+    sh = rettn.shape(1, 1, 128, 64, 64, 1)
+    p = ctypes.c_void_p(4096)
+    st = lib.rt_select_blocks(ctypes.byref(sh), p, p, None, 0, p, None, p, 1 << 20, None)
+    assert st == rettn.RT_E_DEVICE

@@ -1,0 +1,403 @@
+"""GPU parity of the HIP path (through the C ABI) against the oracle."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_diffusion_amd import configs, rettn, synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+def small_cfg(name, **over):
+    c = dict(configs.CONFIGS[name])
+    c.update(over)
+    return c
+
+
+# ------------------------------------------------------------------ selector
+def block_constant_inputs(B, H, N, D, seed, dtype):
+    """q, k constant inside every 64-token block with small integer entries, so
+    pooled means and pooled logits (scale 1/8 for d = 64) are exact in float32
+    on both sides, with many exact ties."""
+    g = torch.Generator().manual_seed(seed)
+    nb = (N + 63) // 64
+    out = []
+    for _ in range(2):
+        vals = torch.randint(-2, 3, (B, H, nb, D), generator=g).float()
+        x = vals.repeat_interleave(64, dim=2)[:, :, :N]
+        out.append(x.to(torch.bfloat16 if dtype == "bf16" else torch.float32))
+    return out
+
+
+@pytest.mark.parametrize("N,keep,forced,dtype", [
+    (1000, 5, [0, 7], "bf16"), (256, 2, [], "f32"), (64 * 37 + 5, 9, [0, 1, 2, 3], "bf16"),
+    (65536, 9, [0, 1, 2, 3], "bf16"), (640, 10, [], "bf16"), (130, 1, [2], "bf16"),
+])
+def test_selector_exact_on_exact_scores(N, keep, forced, dtype):
+    say("selector exact", N, keep, forced, dtype)
+    B, H, D = 1, 2, 64
+    q, k = block_constant_inputs(B, H, N, D, seed=N, dtype=dtype)
+    sh = rettn.shape(B, H, N, 64, D, keep, dtype)
+    idx, scores = gu.select(sh, q.to(gu.DEV), k.to(gu.DEV), forced)
+    ref_scores = oracle.pooled_scores(gu.host(q), gu.host(k), N, 64)
+    assert np.array_equal(scores.cpu().numpy().astype(np.float64), ref_scores)
+    ref = oracle.select_blocks(gu.host(q), gu.host(k), N, 64, keep, forced)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("name", ["tiny", "pixart512", "pixart1024", "cogvideox2b"])
+def test_selector_on_workload(name):
+    say("selector workload", name)
+    cfg = configs.CONFIGS[name]
+    sh = rettn.shape_of(cfg)
+    forced = configs.forced_blocks(cfg)
+    (q, k, v), = gu.gpu_inputs(cfg, 1)
+    idx, scores = gu.select(sh, q, k, forced)
+    idx, scores = idx.cpu().numpy(), scores.cpu().numpy()
+    # the GPU list is a valid top-k of the GPU's own exported scores
+    B, H, nb, _ = idx.shape
+    for b in range(B):
+        for h in range(H):
+            for i in range(nb):
+                assert gu.valid_topk(scores[b, h, i], idx[b, h, i], cfg["keep"], forced), (b, h, i)
+    # against the oracle's float64 scores: disagreements only at near-ties
+    ref_scores = oracle.pooled_scores(gu.host(q), gu.host(k), cfg["N"], cfg["d"])
+    ref = oracle.select_blocks(None, None, cfg["N"], cfg["d"], cfg["keep"], forced, scores=ref_scores)
+    n_diff = 0
+    for b in range(B):
+        for h in range(H):
+            for i in range(nb):
+                a, r = set(idx[b, h, i]), set(ref[b, h, i])
+                if a == r:
+                    continue
+                n_diff += 1
+                tau = min(ref_scores[b, h, i, j] for j in r if j not in forced)
+                for j in a ^ r:
+                    assert abs(ref_scores[b, h, i, j] - tau) < 1e-5, (b, h, i, j)
+    assert n_diff <= max(1, B * H * nb // 1000)
+
+
+# ------------------------------------------------------------------ attention
+def run_full_parity(cfg, steps_to_check, seed=0):
+    """Oracle lists fed to the GPU; calibrate at step 0, reshape at later steps;
+    the full layer is compared."""
+    sh = rettn.shape_of(cfg)
+    N, d = cfg["N"], cfg["d"]
+    forced = configs.forced_blocks(cfg)
+    n_steps = max(steps_to_check) + 1
+    stepsin = gu.gpu_inputs(cfg, n_steps, seed)
+    q0, k0, v0 = stepsin[0]
+    ref_idx = gu.oracle_lists(cfg, q0, k0, forced, cfg["keep"])
+    idx = torch.as_tensor(ref_idx).to(gu.DEV)
+    cache = rettn.StatsCache(sh, 1)
+    o_cal = gu.calibrate(sh, q0, k0, v0, idx, cache)
+    torch.cuda.synchronize()
+    ref_cal = oracle.calibrate(gu.host(q0), gu.host(k0), gu.host(v0), ref_idx, N, d)
+    tol = dict(max_rel=1e-5, l1_rel=1e-6) if cfg["dtype"] == "f32" else {}
+    res = {"calibrate": gu.assert_close(gu.host(o_cal), ref_cal["o"], what="calibrate O", **tol)}
+    t = cache.tensors(0)
+    assert np.array_equal(t["idx"].cpu().numpy(), ref_idx)
+    assert np.abs(gu.host(t["m"]) - ref_cal["m"]).max() <= 1e-4 * max(1.0, np.abs(ref_cal["m"]).max())
+    for zname in ("z_full", "z_sparse"):
+        zr = np.abs(gu.host(t[zname]) / ref_cal[zname] - 1).max()
+        assert zr <= 1e-4, (zname, zr)
+    r_l1 = np.abs(gu.host(t["R"]) - ref_cal["r"]).sum() / max(1e-30, np.abs(ref_cal["r"]).sum())
+    assert r_l1 <= 3e-3, r_l1
+    for s in steps_to_check:
+        q, k, v = stepsin[s]
+        o = gu.sparse(sh, q, k, v, cache)
+        torch.cuda.synchronize()
+        ref_o = oracle.sparse_reshape(gu.host(q), gu.host(k), gu.host(v), ref_idx, ref_cal, N, d)
+        res[f"step{s}"] = gu.assert_close(gu.host(o), ref_o, what=f"step {s} O", **tol)
+    cache.close()
+    return res
+
+
+def test_parity_tiny_f32():
+    say("parity tiny f32")
+    run_full_parity(configs.CONFIGS["tiny"], [1])
+
+
+def test_parity_pixart512():
+    say("parity pixart512")
+    run_full_parity(configs.CONFIGS["pixart512"], [1, 9])
+
+
+def test_parity_pixart1024():
+    say("parity pixart1024")
+    run_full_parity(configs.CONFIGS["pixart1024"], [1, 19])
+
+
+def run_sampled_parity(cfg, heads, seed=0, n_steps=2, check_steps=(1,)):
+    """Full-size layers: the GPU runs every row; the oracle checks sampled query
+    blocks (first, text/video boundary, middle, ragged last) of sampled heads."""
+    sh = rettn.shape_of(cfg)
+    N, d, keep = cfg["N"], cfg["d"], cfg["keep"]
+    forced = configs.forced_blocks(cfg)
+    nb = configs.n_blocks(N)
+    it = synth.StepInputs(cfg, seed=seed, device=gu.DEV)
+    q0, k0, v0 = (synth.store(x, cfg["dtype"]) for x in it.next())
+    ref_idx = np.zeros((sh.B, sh.H, nb, keep), dtype=np.int32)
+    hq, hk = {}, {}
+    for b, h in heads:
+        hq[b, h] = gu.host(q0[b, h][None, None])
+        hk[b, h] = gu.host(k0[b, h][None, None])
+    # oracle lists for every head (pooling is cheap), so the GPU input is all-oracle
+    for b in range(sh.B):
+        for h in range(sh.H):
+            qq, kk = gu.host(q0[b, h][None, None]), gu.host(k0[b, h][None, None])
+            ref_idx[b, h] = oracle.select_blocks(qq, kk, N, d, keep, forced)[0, 0]
+    idx = torch.as_tensor(ref_idx).to(gu.DEV)
+    cache = rettn.StatsCache(sh, 1)
+    o_cal = gu.calibrate(sh, q0, k0, v0, idx, cache)
+    torch.cuda.synchronize()
+    t = cache.tensors(0)
+    cal_host = {bh: [gu.host(x[bh[0], bh[1]]) for x in (q0, k0, v0)] for bh in heads}
+    blocks = gu.sample_blocks(nb)
+    refs = {}
+    for (b, h) in heads:
+        qh, kh, vh = cal_host[b, h]
+        for i in blocks:
+            rows = gu.block_rows(N, i)
+            st = oracle.calibrate_rows(qh, kh, vh, rows, ref_idx[b, h, i], N, d)
+            refs[b, h, i] = st
+            gu.assert_close(gu.host(o_cal[b, h, rows]), st["o"], what=f"cal O b{b} h{h} blk{i}")
+            assert np.abs(gu.host(t["m"][b, h, rows]) - st["m"]).max() <= 1e-4 * max(1, np.abs(st["m"]).max())
+            assert np.abs(gu.host(t["z_full"][b, h, rows]) / st["z_full"] - 1).max() <= 1e-4
+            assert np.abs(gu.host(t["z_sparse"][b, h, rows]) / st["z_sparse"] - 1).max() <= 1e-4
+            rl1 = np.abs(gu.host(t["R"][b, h, rows]) - st["r"]).sum() / np.abs(st["r"]).sum()
+            assert rl1 <= 3e-3, rl1
+    for s in range(1, n_steps):
+        q, k, v = (synth.store(x, cfg["dtype"]) for x in it.next())
+        if s not in check_steps:
+            continue
+        o = gu.sparse(sh, q, k, v, cache)
+        torch.cuda.synchronize()
+        for (b, h) in heads:
+            qh, kh, vh = (gu.host(x[b, h]) for x in (q, k, v))
+            for i in blocks:
+                rows = gu.block_rows(N, i)
+                st = refs[b, h, i]
+                ro = oracle.sparse_reshape_rows(qh, kh, vh, rows, ref_idx[b, h, i], st["m"], st["z_full"],
+                                                st["z_sparse"], st["r"], N, d)
+                gu.assert_close(gu.host(o[b, h, rows]), ro, what=f"step {s} O b{b} h{h} blk{i}")
+    cache.close()
+
+
+def test_parity_cogvideox2b_sampled():
+    say("parity cogvideox2b sampled")
+    cfg = configs.CONFIGS["cogvideox2b"]
+    run_sampled_parity(cfg, heads=[(0, 0), (1, 29)], n_steps=4, check_steps=(1, 3))
+
+
+# ------------------------------------------------------------------ identities on the GPU
+@pytest.mark.parametrize("name", ["pixart512", "pixart1024"])
+def test_gpu_calibration_identity(name):
+    """Calibrate then reshape on the same inputs gives dense attention."""
+    say("calibration identity", name)
+    cfg = configs.CONFIGS[name]
+    sh = rettn.shape_of(cfg)
+    (q, k, v), = gu.gpu_inputs(cfg, 1, seed=3)
+    idx, _ = gu.select(sh, q, k, configs.forced_blocks(cfg))
+    cache = rettn.StatsCache(sh, 1)
+    gu.calibrate(sh, q, k, v, idx, cache)
+    o = gu.sparse(sh, q, k, v, cache)
+    torch.cuda.synchronize()
+    dense = oracle.dense_attention(gu.host(q), gu.host(k), gu.host(v), cfg["N"], cfg["d"])
+    gu.assert_close(gu.host(o), dense)
+
+
+def test_gpu_keep_all_identity():
+    """keep = Nb: zero residual, equal denominators, dense output at later steps."""
+    say("keep-all identity")
+    cfg = small_cfg("pixart512", H=4, keep=16)
+    sh = rettn.shape_of(cfg)
+    stepsin = gu.gpu_inputs(cfg, 4, seed=4)
+    q0, k0, v0 = stepsin[0]
+    idx, _ = gu.select(sh, q0, k0, [])
+    assert np.array_equal(idx.cpu().numpy()[0, 0, 0], np.arange(16))
+    cache = rettn.StatsCache(sh, 1)
+    gu.calibrate(sh, q0, k0, v0, idx, cache)
+    torch.cuda.synchronize()
+    t = cache.tensors(0)
+    assert float(t["R"].abs().max()) == 0.0
+    assert torch.equal(t["z_full"], t["z_sparse"])
+    q, k, v = stepsin[3]
+    o = gu.sparse(sh, q, k, v, cache)
+    torch.cuda.synchronize()
+    gu.assert_close(gu.host(o), oracle.dense_attention(gu.host(q), gu.host(k), gu.host(v), cfg["N"], cfg["d"]))
+
+
+@pytest.mark.parametrize("name", ["pixart512", "pixart1024"])
+def test_sparse_kernel_with_oracle_cache(name):
+    """The sparse kernel alone, fed statistics and lists made by the oracle."""
+    say("sparse kernel with oracle cache", name)
+    cfg = configs.CONFIGS[name]
+    sh = rettn.shape_of(cfg)
+    N, d = cfg["N"], cfg["d"]
+    (q0, k0, v0), (q1, k1, v1) = gu.gpu_inputs(cfg, 2, seed=5)
+    ref_idx = gu.oracle_lists(cfg, q0, k0, [], cfg["keep"])
+    ref_cal = oracle.calibrate(gu.host(q0), gu.host(k0), gu.host(v0), ref_idx, N, d)
+    cache = rettn.StatsCache(sh, 1)
+    t = cache.tensors(0)
+    for name_ in ("m", "z_full", "z_sparse"):
+        t[name_].copy_(torch.as_tensor(ref_cal[name_], dtype=torch.float32))
+    t["R"].copy_(torch.as_tensor(ref_cal["r"], dtype=torch.float32))
+    t["idx"].copy_(torch.as_tensor(ref_idx))
+    cache.set_valid(0)
+    o = gu.sparse(sh, q1, k1, v1, cache)  # lists from the cache
+    torch.cuda.synchronize()
+    ref = oracle.sparse_reshape(gu.host(q1), gu.host(k1), gu.host(v1), ref_idx, ref_cal, N, d)
+    gu.assert_close(gu.host(o), ref)
+    o2 = gu.sparse(sh, q1, k1, v1, cache, idx=torch.as_tensor(ref_idx).to(gu.DEV))  # explicit lists
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+
+
+# ------------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("N,d,D,keep,forced,dtype", [
+    (64, 64, 64, 1, [], "bf16"),        # one block
+    (40, 64, 64, 1, [], "bf16"),        # one short block
+    (100, 64, 64, 2, [], "bf16"),       # keep all, ragged
+    (200, 64, 64, 1, [3], "bf16"),      # only the forced (short, last) block kept
+    (333, 72, 80, 3, [1], "bf16"),      # padded head dim, ragged
+    (333, 8, 64, 2, [], "bf16"),        # tiny true head dim
+    (130, 64, 64, 2, [0], "f32"),
+    (333, 72, 80, 2, [], "f32"),
+])
+def test_edge_shapes(N, d, D, keep, forced, dtype):
+    say("edge", N, d, D, keep, forced, dtype)
+    B, H = 2, 3
+    q0, k0, v0 = synth.random_qkv(B, H, N, d, D, seed=N + d, scale=1.5, dtype=dtype, device=gu.DEV)
+    q1, k1, v1 = synth.random_qkv(B, H, N, d, D, seed=N + d + 1, scale=1.5, dtype=dtype, device=gu.DEV)
+    sh = rettn.shape(B, H, N, d, D, keep, dtype)
+    ref_idx = oracle.select_blocks(gu.host(q0), gu.host(k0), N, d, keep, forced)
+    idx, _ = gu.select(sh, q0, k0, forced)
+    cache = rettn.StatsCache(sh, 1)
+    o_cal = gu.calibrate(sh, q0, k0, v0, torch.as_tensor(ref_idx).to(gu.DEV), cache)
+    o = gu.sparse(sh, q1, k1, v1, cache)
+    torch.cuda.synchronize()
+    ref_cal = oracle.calibrate(gu.host(q0), gu.host(k0), gu.host(v0), ref_idx, N, d)
+    ref = oracle.sparse_reshape(gu.host(q1), gu.host(k1), gu.host(v1), ref_idx, ref_cal, N, d)
+    tol = dict(max_rel=1e-5, l1_rel=1e-6) if dtype == "f32" else {}
+    gu.assert_close(gu.host(o_cal), ref_cal["o"], what="calibrate", **tol)
+    gu.assert_close(gu.host(o), ref, what="sparse", **tol)
+    if D > d:
+        assert float(o[..., d:].abs().max()) == 0.0 and float(o_cal[..., d:].abs().max()) == 0.0
+    # the GPU selector agrees with the oracle on these random inputs (no near-ties expected)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+
+
+def test_deterministic_bitwise():
+    say("determinism")
+    cfg = small_cfg("pixart1024", H=4)
+    sh = rettn.shape_of(cfg)
+    (q0, k0, v0), (q1, k1, v1) = gu.gpu_inputs(cfg, 2, seed=6)
+    outs = []
+    for _ in range(2):
+        idx, sc = gu.select(sh, q0, k0, [])
+        cache = rettn.StatsCache(sh, 1)
+        oc = gu.calibrate(sh, q0, k0, v0, idx, cache)
+        o = gu.sparse(sh, q1, k1, v1, cache)
+        torch.cuda.synchronize()
+        t = cache.tensors(0)
+        outs.append([idx, sc, oc, o, t["m"].clone(), t["z_full"].clone(), t["z_sparse"].clone(), t["R"].clone()])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ schedule through the ABI
+def test_schedule_pixart512_through_attention_step():
+    say("schedule pixart512")
+    cfg = configs.CONFIGS["pixart512"]
+    sh = rettn.shape_of(cfg)
+    N, d = cfg["N"], cfg["d"]
+    stepsin = gu.gpu_inputs(cfg, cfg["steps"], seed=7)
+    cache = rettn.StatsCache(sh, 1)
+    ws = torch.empty(rettn.step_workspace_bytes(sh), dtype=torch.uint8, device=gu.DEV)
+    q0, k0, v0 = stepsin[0]
+    ref_idx = gu.oracle_lists(cfg, q0, k0, [], cfg["keep"])
+    ref_cal = None
+    for s, (q, k, v) in enumerate(stepsin):
+        o = gu.empty_out(sh)
+        did = rettn.rt_attention_step(sh, q, k, v, [], cache, 0, s, 0, o, ws)
+        torch.cuda.synchronize()
+        assert did == (s == 0)
+        if s == 0:
+            gpu_idx = cache.tensors(0)["idx"].cpu().numpy()
+            assert np.array_equal(gpu_idx, ref_idx)
+            ref_cal = oracle.calibrate(gu.host(q), gu.host(k), gu.host(v), ref_idx, N, d)
+            ref = ref_cal["o"]
+        else:
+            ref = oracle.sparse_reshape(gu.host(q), gu.host(k), gu.host(v), ref_idx, ref_cal, N, d)
+        gu.assert_close(gu.host(o), ref, what=f"step {s}")
+
+
+def test_cogvideox5b_layers_and_recalibration():
+    """42 layers share one cache allocation; layers 0 and 41 run a 12-step
+    schedule with recalibration every 10 steps; sampled rows of the
+    recalibration step and the step after it are checked."""
+    say("cogvideox5b 42-layer cache")
+    cfg = configs.CONFIGS["cogvideox5b"]
+    sh = rettn.shape_of(cfg)
+    N, d, keep = cfg["N"], cfg["d"], cfg["keep"]
+    forced = configs.forced_blocks(cfg)
+    nb = configs.n_blocks(N)
+    cache = rettn.StatsCache(sh, cfg["layers"])
+    ws = torch.empty(rettn.step_workspace_bytes(sh), dtype=torch.uint8, device=gu.DEV)
+    heads = [(0, 0), (1, 47)]
+    blocks = gu.sample_blocks(nb)
+    for layer in (0, cfg["layers"] - 1):
+        it = synth.StepInputs(cfg, seed=1000 + layer, device=gu.DEV)
+        cal_inputs = None
+        for s in range(12):
+            q, k, v = (synth.store(x, cfg["dtype"]) for x in it.next())
+            if s < 9:
+                continue
+            o = gu.empty_out(sh)
+            did = rettn.rt_attention_step(sh, q, k, v, forced, cache, layer, s, cfg["period"], o, ws)
+            torch.cuda.synchronize()
+            assert did == (s == 10)
+            if s == 9:
+                continue
+            if s == 10:
+                cal_inputs = {bh: [gu.host(x[bh[0], bh[1]]) for x in (q, k, v)] for bh in heads}
+                lists = cache.tensors(layer)["idx"].cpu().numpy()
+            for (b, h) in heads:
+                qc, kc, vc = cal_inputs[b, h]
+                ref_scores = oracle.pooled_scores(qc[None, None], kc[None, None], N, d)[0, 0]
+                for i in blocks:
+                    ref_list = oracle.select_from_scores(ref_scores[i], keep, forced)
+                    if set(lists[b, h, i]) != set(ref_list):  # only a near-tie may differ
+                        tau = min(ref_scores[i, j] for j in ref_list if j not in forced)
+                        assert all(abs(ref_scores[i, j] - tau) < 1e-5 for j in set(lists[b, h, i]) ^ set(ref_list))
+                        continue
+                    rows = gu.block_rows(N, i)
+                    st = oracle.calibrate_rows(qc, kc, vc, rows, ref_list, N, d)
+                    if s == 10:
+                        gu.assert_close(gu.host(o[b, h, rows]), st["o"], what=f"L{layer} s10 b{b}h{h}i{i}")
+                    else:
+                        qh, kh, vh = (gu.host(x[b, h]) for x in (q, k, v))
+                        ro = oracle.sparse_reshape_rows(qh, kh, vh, rows, ref_list, st["m"], st["z_full"],
+                                                        st["z_sparse"], st["r"], N, d)
+                        gu.assert_close(gu.host(o[b, h, rows]), ro, what=f"L{layer} s11 b{b}h{h}i{i}")
+    views = [cache.tensors(layer) for layer in (0, 1, cfg["layers"] - 1)]
+    assert views[0]["valid"] == 1 and views[1]["valid"] == 0 and views[2]["valid"] == 1
+    assert not torch.equal(views[0]["m"], views[2]["m"])
