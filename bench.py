@@ -38,7 +38,9 @@ def parse():
     p.add_argument("--denoise-steps", type=int, default=None, help="override the schedule length")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=2)
-    p.add_argument("--cpu-budget-s", type=float, default=20.0)
+    p.add_argument("--cpu-budget-s", type=float, default=10.0)
+    p.add_argument("--traffic-probe", action="store_true",
+                   help="first run a plain 512 MiB device copy (reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -146,6 +148,14 @@ def main():
     forced = configs.forced_blocks(cfg)
     nsteps = cfg["steps"]
     period = cfg["period"] or 0
+
+    if args.traffic_probe:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # inputs of every denoising step resident in HBM
     it = synth.StepInputs(cfg, seed=0, device=dev)

@@ -23,6 +23,8 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     # packed fp32 instructions are kept out of all generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators live in VGPRs (no AGPR<->VGPR copies around the softmax)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -8,359 +8,652 @@
 // paragraph); the sparse step attends to the kept key blocks only and rescales
 // its result with those cached statistics (teaser paragraph).
 //
-// Work decomposition.  One workgroup = one 64-row query block of one (b, h);
-// two waves of 32 rows each.  Per key block (64 keys) a wave computes
+// Per wave: 32 query rows.  Per key block (64 keys) a wave computes
 //   S^T (64 keys x 32 rows) = K . Q^T   with v_mfma_f32_32x32x16_bf16, and
 //   O^T (D x 32 rows)      += V^T . P^T  with the same instruction,
-// so that every lane owns one query row (lane % 32) in both results and the
-// row statistics never leave the lane (only lanes l and l^32 exchange the max).
-// K and V tiles are staged in LDS (XOR-swizzled 16-byte units); V^T operands
-// are read with ds_read_b64_tr_b16.  Calibration processes the kept blocks
-// first, snapshots that partial result, then accumulates the masked blocks:
-// one pass, one running max, no second accumulator inside the loop.
+// so every lane owns one query row (lane % 32) in both results and the row
+// statistics never leave the lane pair (l, l^32).
+//
+// K and V tiles reach LDS by DMA (global_load_lds_dwordx4, no register
+// staging) into a ring of NBUF slots, so NBUF-1 key blocks are in flight while
+// one is consumed; one workgroup barrier per key block.  LDS rows are made of
+// 16-byte units, XOR-swizzled.  All LDS reads of the ring are issued from
+// inline asm that waits for them itself: the compiler would otherwise wait for
+// every DMA in flight before each read (it cannot tell ring slots apart), which
+// would undo the prefetch.  V^T operands come from ds_read_b64_tr_b16.  The
+// softmax reference max is raised lazily (only when a block max exceeds it by
+// more than a factor 2^8 in probability), which keeps the accumulator rescale
+// off the common path.
+//
+// Sparse kernel: one workgroup (2 waves) per 64-row query block; the cached
+// residual and statistics are prefetched into registers at entry.
+// Calibration kernel: QB query blocks (2 waves each) share every K/V tile; key
+// blocks are visited in ascending order and each wave adds a block either to
+// its kept accumulator or to its residual accumulator (a wave-uniform choice).
 #include "internal.h"
 
 namespace rettn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kThreads = 128;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyLog2 = 8.f;  // raise the reference max only past a factor 2^8
 
 template <int D>
 struct Shape {
   static constexpr int KS = D / 16;             // k-steps of the d contraction
   static constexpr int NT = (D + 31) / 32;      // 32-wide d tiles of O^T
   static constexpr int UNITS = D / 8;           // 16-byte units per row in HBM
-  static constexpr int RSU = D == 64 ? 8 : 12;  // LDS row stride in units (80: 2 zero units)
-  static constexpr int TILE = kBlock * RSU * 16;
-  static constexpr int PER_THREAD = kBlock * UNITS / kThreads;
+  static constexpr int RSU = D == 64 ? 8 : 12;  // LDS row stride in units (80: 2 filler units)
+  static constexpr int ROW = RSU * 16;          // LDS row stride in bytes
+  static constexpr int TILE = kBlock * ROW;     // bytes of one K (or V) tile
+  static constexpr int SLOT = 2 * TILE;         // K tile then V tile
   static_assert(D == 64 || D == 80, "head dim");
-  static_assert(kBlock * UNITS % kThreads == 0, "tile split");
 };
+
+// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Waits until the tile of this step has landed, allowing `younger` later tiles
+// (IPT DMA instructions each) to stay in flight.  Any other memory operation
+// issued after the tile only makes the wait longer, never too short.
+template <int IPT>
+__device__ __forceinline__ void wait_tile(int younger) {
+  if (younger >= 2) wait_vmcnt<2 * IPT>();
+  else if (younger == 1) wait_vmcnt<IPT>();
+  else wait_vmcnt<0>();
+}
 
 // Physical 16-byte unit of logical unit u in LDS row r.  Units 0..7 are
 // XOR-swizzled so that 16 consecutive rows read at one unit, and 4 consecutive
 // rows read at 4 aligned units, fall in distinct bank groups.
-__device__ __forceinline__ int phys_unit(int r, int u) {
-  int f = (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-  return u < 8 ? (u ^ f) : u;
-}
+__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int phys_unit(int r, int u) { return u < 8 ? (u ^ swz(r)) : u; }
 
 template <int D>
 __device__ __forceinline__ int lds_off(int r, int u) {
-  return (r * Shape<D>::RSU + phys_unit(r, u)) * 16;
+  return r * Shape<D>::ROW + phys_unit(r, u) * 16;
 }
 
-template <int D>
-struct Tile {
-  u32x4 k[Shape<D>::PER_THREAD];
-  u32x4 v[Shape<D>::PER_THREAD];
-};
-
-// Global -> registers for key block j (rows past N are clamped to row N-1;
-// their scores are masked later, so only finiteness matters).
-template <int D>
-__device__ __forceinline__ void load_tile(Tile<D>& t, const char* kbase, const char* vbase, int j, int N) {
-  constexpr int U = Shape<D>::UNITS;
-#pragma unroll
-  for (int n = 0; n < Shape<D>::PER_THREAD; ++n) {
-    int e = threadIdx.x + n * kThreads;
-    int r = e / U, u = e % U;
-    int key = min(j * kBlock + r, N - 1);
-    size_t off = ((size_t)key * D + u * 8) * 2;
-    t.k[n] = *(const u32x4*)(kbase + off);
-    t.v[n] = *(const u32x4*)(vbase + off);
-  }
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-template <int D>
-__device__ __forceinline__ void store_tile(const Tile<D>& t, char* lk, char* lv) {
-  constexpr int U = Shape<D>::UNITS;
-#pragma unroll
-  for (int n = 0; n < Shape<D>::PER_THREAD; ++n) {
-    int e = threadIdx.x + n * kThreads;
-    int r = e / U, u = e % U;
-    *(u32x4*)(lk + lds_off<D>(r, u)) = t.k[n];
-    *(u32x4*)(lv + lds_off<D>(r, u)) = t.v[n];
-  }
-}
+// ------------------------------------------------------------------ DMA of tiles
+// A tile pair (K and V of one key block) is 2*RSU DMA instructions of 1 KB
+// (64 lanes x 16 B).  Wave w of W takes the K instructions c = w, w+W, ... and
+// the same c for V (W divides RSU).  Lane l of instruction c fills LDS unit
+// 64c + l of the tile, i.e. (row, physical unit), and fetches the logical unit
+// the swizzle puts there.  The per-lane source offsets are computed once.
+template <int D, int W>
+struct TileDma {
+  static constexpr int RSU = Shape<D>::RSU;
+  static_assert(RSU % W == 0, "waves must divide the row units");
+  static constexpr int NI = RSU / W;  // K (and V) instructions per wave
+  static constexpr int IPT = 2 * NI;  // DMA instructions per tile per wave
+  uint32_t off[NI];
+  int row[NI];
+  int wave;
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
-
-template <int D>
-struct WaveState {
-  bf16x8 q[Shape<D>::KS];      // Q^T operand: row lane%32, d = 16s + 8g + 0..7
-  f32x16 o[Shape<D>::NT];      // O^T accumulator: row lane%32, d = 32t + 8(i/4) + 4g + i%4
-  float m_raw;                 // running max of raw scores q.k (common to lanes l, l^32)
-  float z;                     // this lane's partial denominator (its half of the keys)
-};
-
-// One key block for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
-template <int D>
-__device__ __forceinline__ void attend_block(WaveState<D>& st, const char* lk, const char* lv, int nvalid,
-                                             float c) {
-  constexpr int KS = Shape<D>::KS, NT = Shape<D>::NT;
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 5, l32 = lane & 31;
-  f32x16 s[2];
+  __device__ __forceinline__ void init(int w, int lane) {
+    wave = w;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    s[t] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 a = *(const bf16x8*)(lk + lds_off<D>(32 * t + l32, 2 * ks + g));
-      s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.q[ks], s[t], 0, 0, 0);
+    for (int i = 0; i < NI; ++i) {
+      const int L = 64 * (w + W * i) + lane;
+      const int r = L / RSU, p = L % RSU;
+      int u = p < 8 ? (p ^ swz(r)) : p;
+      if (u >= Shape<D>::UNITS) u -= 2;  // filler units of d_pad = 80 rows: any finite data
+      row[i] = r;
+      off[i] = (uint32_t)((r * D + u * 8) * 2);
     }
   }
-  if (nvalid < kBlock) {  // ragged last key block: keys >= N do not exist
+  // Key block j of the head at (kbase, vbase) into the slot at `slot`; keys
+  // past N read row N-1 (finite data; their scores are masked).
+  __device__ __forceinline__ void issue(char* slot, const char* kbase, const char* vbase, int j, int N) const {
+    const size_t blk = (size_t)j * kBlock * D * 2;
+    const int nvalid = N - j * kBlock;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      uint32_t o = off[i];
+      if (nvalid < kBlock) o -= (uint32_t)(max(0, row[i] - (nvalid - 1)) * D * 2);
+      char* dst = slot + (wave + W * i) * 1024;
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + blk + o), (lds_void*)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vbase + blk + o), (lds_void*)(dst + Shape<D>::TILE), 16, 0,
+                                       0);
+    }
+  }
+};
+
+// ------------------------------------------------------------------ LDS reads (asm)
+// Per-lane LDS addresses of the MFMA operands in ring slot 0; other slots and
+// the second 32-key half are compile-time offsets.
+template <int D>
+struct Frag {
+  uint32_t k[Shape<D>::KS];     // K operand, key half t = 0, k-step ks
+  uint32_t v[Shape<D>::NT][2];  // V^T operand, d tile dt, half hh, k-step (t, hs) = (0, 0)
+  __device__ __forceinline__ void init(const char* ring) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 5, l32 = lane & 31, G = lane >> 4, i16 = lane & 15;
+    const uint32_t base = lds_addr(ring);
+#pragma unroll
+    for (int ks = 0; ks < Shape<D>::KS; ++ks) k[ks] = base + lds_off<D>(l32, 2 * ks + g);
+#pragma unroll
+    for (int dt = 0; dt < Shape<D>::NT; ++dt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        // ds_read_b64_tr_b16 transposes within 16-lane groups: lane i of a group
+        // points at key kbase + i/4, columns 4(i%4)..+3, and receives column i of
+        // keys kbase..kbase+3.  t and hs move whole 16-key groups (no swizzle change).
+        const int key = 8 * hh + 4 * g + (i16 >> 2);
+        const int doff = 32 * dt + 16 * (G & 1) + 4 * (i16 & 3);
+        v[dt][hh] = base + Shape<D>::TILE + lds_off<D>(key, doff >> 3) + (doff & 7) * 2;
+      }
+  }
+};
+
+// K operands of one 32-key half: KS ds_read_b128, waited for in the same statement.
+template <int KS, int OFF>
+__device__ __forceinline__ void k_reads(u32x4 (&a)[KS], const uint32_t (&ad)[KS]) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  if constexpr (KS == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:%8\n\t"
+        "ds_read_b128 %1, %5 offset:%8\n\t"
+        "ds_read_b128 %2, %6 offset:%8\n\t"
+        "ds_read_b128 %3, %7 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "i"(OFF)
+        : "memory");
+  } else {
+    static_assert(KS == 5, "k-steps");
+    asm volatile(
+        "ds_read_b128 %0, %5 offset:%10\n\t"
+        "ds_read_b128 %1, %6 offset:%10\n\t"
+        "ds_read_b128 %2, %7 offset:%10\n\t"
+        "ds_read_b128 %3, %8 offset:%10\n\t"
+        "ds_read_b128 %4, %9 offset:%10\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "i"(OFF)
+        : "memory");
+  }
+}
+
+// V^T operands of one d tile for the four k-steps (t, hs): eight
+// ds_read_b64_tr_b16, waited for in the same statement.  h[t][hs][hh].
+template <int OFF, int T, int HS>
+__device__ __forceinline__ void tr_reads(u32x2 (&h)[2][2][2], uint32_t a0, uint32_t a1) {
+  static_assert(OFF + T + HS < 65536, "ds offset");
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%10\n\t"
+      "ds_read_b64_tr_b16 %1, %9 offset:%10\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:%11\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:%11\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %5, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %6, %8 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %7, %9 offset:%13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(h[0][0][0]), "=&v"(h[0][0][1]), "=&v"(h[0][1][0]), "=&v"(h[0][1][1]), "=&v"(h[1][0][0]),
+        "=&v"(h[1][0][1]), "=&v"(h[1][1][0]), "=&v"(h[1][1][1])
+      : "v"(a0), "v"(a1), "i"(OFF), "i"(OFF + HS), "i"(OFF + T), "i"(OFF + T + HS)
+      : "memory");
+}
+
+// ------------------------------------------------------------------ per-block math
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D>
+struct Rows {
+  bf16x8 q[Shape<D>::KS];  // Q^T operand: row lane%32, d = 16s + 8g + 0..7
+  float m_ref;             // reference max (raw q.k units) the exponentials are taken against
+  float m_true;            // running max of raw scores
+};
+
+// S^T = K Q^T for the key block in the slot at byte offset SLOT_OFF; keys at
+// or past nvalid are set to -inf.  s[t][i] is key 32t + 8(i/4) + 4g + i%4.
+template <int D, int OFF>
+__device__ __forceinline__ f32x16 scores_half(const Rows<D>& st, const Frag<D>& fr) {
+  constexpr int KS = Shape<D>::KS;
+  u32x4 a[KS];
+  k_reads<KS, OFF>(a, fr.k);
+  f32x16 s = {};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[ks]), st.q[ks], s, 0, 0, 0);
+  return s;
+}
+
+template <int D, int SLOT_OFF>
+__device__ __forceinline__ void scores(f32x16 (&s)[2], const Rows<D>& st, const Frag<D>& fr, int nvalid) {
+  s[0] = scores_half<D, SLOT_OFF>(st, fr);
+  s[1] = scores_half<D, SLOT_OFF + 32 * Shape<D>::ROW>(st, fr);
+  if (nvalid < kBlock) {
+    const int g = (threadIdx.x & 63) >> 5;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        int key = 32 * t + (i >> 2) * 8 + 4 * g + (i & 3);
+        const int key = 32 * t + (i >> 2) * 8 + 4 * g + (i & 3);
         if (key >= nvalid) s[t][i] = -INFINITY;
       }
   }
+}
+
+__device__ __forceinline__ float row_max(const f32x16 (&s)[2]) {
   float mx = -INFINITY;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
-  mx = fmaxf(mx, xor32(mx));
-  const float m_new = fmaxf(st.m_raw, mx);
-  if (__ballot(m_new > st.m_raw) != 0ull) {
-    const float corr = st.m_raw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m_raw - m_new) * c);
-    st.z *= corr;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) st.o[t][i] *= corr;
-    st.m_raw = m_new;
+  return pair_max(mx);
+}
+
+// Raises the reference max when some row of the wave needs it; returns the
+// factor the accumulators must be multiplied by, and whether any changed.
+__device__ __forceinline__ float update_max(float& m_ref, float& m_true, float mx, float c, bool* any) {
+  m_true = fmaxf(m_true, mx);
+  const bool need = mx > m_ref + kLazyLog2 / c;
+  *any = __ballot(need) != 0ull;
+  float corr = 1.f;
+  if (*any) {
+    const float m_new = fmaxf(m_ref, mx);
+    corr = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
+    m_ref = m_new;
   }
-  const float mc = m_new * c;
-  bf16x8 p[2][2];
+  return corr;
+}
+
+// P = exp2(c s - c m_ref) as bf16 MFMA operands (p[t][hs] holds k-step (t, hs));
+// returns this lane's float32 sum of P.
+__device__ __forceinline__ float probs(bf16x8 (&p)[2][2], const f32x16 (&s)[2], float m_ref, float c) {
+  const float mc = m_ref * c;
+  float z = 0.f;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float e = __builtin_amdgcn_exp2f(fmaf(s[t][i], c, -mc));
-      st.z += e;
+      const float e = __builtin_amdgcn_exp2f(fmaf(s[t][i], c, -mc));
+      z += e;
       p[t][i >> 3][i & 7] = (__bf16)e;
     }
-  // O^T += V^T P^T.  k-step (t, hs) covers keys 32t + 16hs + 0..15; lane group g
-  // holds slots j <-> key 32t + 16hs + 8(j/4) + 4g + j%4 in both operands.
-  const int G = lane >> 4, i16 = lane & 15;
+  return z;
+}
+
+// This lane's sum of the bf16-rounded P (the values the numerator uses).
+__device__ __forceinline__ float sum_rounded(const bf16x8 (&p)[2][2]) {
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+  float z0 = 0.f, z1 = 0.f;
 #pragma unroll
-  for (int dt = 0; dt < NT; ++dt) {
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bf16x2 lo = {p[t][0][2 * k], p[t][0][2 * k + 1]};
+      const bf16x2 hi = {p[t][1][2 * k], p[t][1][2 * k + 1]};
+      z0 = __builtin_amdgcn_fdot2_f32_bf16(lo, ones, z0, false);
+      z1 = __builtin_amdgcn_fdot2_f32_bf16(hi, ones, z1, false);
+    }
+  return z0 + z1;
+}
+
+// O^T += V^T P^T for the key block in the slot at SLOT_OFF.  k-step (t, hs)
+// covers keys 32t + 16hs + 0..15; lane group g holds slots j <-> key
+// 32t + 16hs + 8(j/4) + 4g + j%4 in both operands.
+template <int D, int SLOT_OFF>
+__device__ __forceinline__ void pv(f32x16 (&o)[Shape<D>::NT], const bf16x8 (&p)[2][2], const Frag<D>& fr) {
+  constexpr int ROW = Shape<D>::ROW;
+#pragma unroll
+  for (int dt = 0; dt < Shape<D>::NT; ++dt) {
+    u32x2 h[2][2][2];
+    tr_reads<SLOT_OFF, 32 * ROW, 16 * ROW>(h, fr.v[dt][0], fr.v[dt][1]);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
-        s16x4 h[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          int key = 32 * t + 16 * hs + 8 * hh + 4 * g + (i16 >> 2);
-          int doff = 32 * dt + 16 * (G & 1) + 4 * (i16 & 3);  // element offset in the row
-          int off = lds_off<D>(key, doff >> 3) + (doff & 7) * 2;
-          h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(lv + off));
-        }
-        const s16x8 both = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, both);
-        st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[t][hs], st.o[dt], 0, 0, 0);
+        const u32x4 both = __builtin_shufflevector(h[t][hs][0], h[t][hs][1], 0, 1, 2, 3);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), p[t][hs], o[dt], 0, 0, 0);
       }
   }
 }
 
-template <int D, AttnMode MODE>
-__global__ void __launch_bounds__(kThreads) attn_bf16_kernel(AttnArgs a, XcdGrid grid) {
-  constexpr int NT = Shape<D>::NT, KS = Shape<D>::KS, TILE = Shape<D>::TILE;
-  __shared__ __attribute__((aligned(16))) char lds_k[TILE + 64];
-  __shared__ __attribute__((aligned(16))) char lds_v[TILE + 64];
+// Q^T operand of this lane's row; rows >= N read row N-1 and are zeroed
+// (every lane issues the same loads).
+template <int D>
+__device__ __forceinline__ void load_q(Rows<D>& st, const char* qbase, int row, int N) {
+  const int g = (threadIdx.x & 63) >> 5;
+  const bool ok = row < N;
+  const size_t r = (size_t)(ok ? row : N - 1);
+#pragma unroll
+  for (int ks = 0; ks < Shape<D>::KS; ++ks) {
+    u32x4 raw = __builtin_nontemporal_load((const u32x4*)(qbase + (r * D + 16 * ks + 8 * g) * 2));
+    if (!ok) raw = u32x4{};
+    st.q[ks] = __builtin_bit_cast(bf16x8, raw);
+  }
+  st.m_ref = -INFINITY;
+  st.m_true = -INFINITY;
+}
+
+// ---------------------------------------------------------------- sparse step
+template <int D, int NBUF>
+struct SparseCtx {
+  static constexpr int NT = Shape<D>::NT;
+  using Dma = TileDma<D, 2>;
+  char* ring;
+  const int* seq;
+  const char* kbase;
+  const char* vbase;
+  int keep, N;
+  float c;
+  Dma dma;
+  Frag<D> fr;
+  Rows<D> st;
+  f32x16 o[NT];
+  float z;
+
+  // Key block n of the list, in ring slot SLOT = n % NBUF.
+  template <int SLOT>
+  __device__ __forceinline__ void step(int n) {
+    wait_tile<Dma::IPT>(min(NBUF - 2, keep - 1 - n));
+    __builtin_amdgcn_s_barrier();
+    if (n + NBUF - 1 < keep) {
+      constexpr int NEXT = (SLOT + NBUF - 1) % NBUF;
+      dma.issue(ring + NEXT * Shape<D>::SLOT, kbase, vbase, __builtin_amdgcn_readfirstlane(seq[n + NBUF - 1]), N);
+    }
+    const int j = __builtin_amdgcn_readfirstlane(seq[n]);
+    f32x16 s[2];
+    scores<D, SLOT * Shape<D>::SLOT>(s, st, fr, min(kBlock, N - j * kBlock));
+    bool any;
+    const float corr = update_max(st.m_ref, st.m_true, row_max(s), c, &any);
+    if (any) {
+      z *= corr;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) o[t] *= corr;
+    }
+    bf16x8 p[2][2];
+    probs(p, s, st.m_ref, c);
+    z += sum_rounded(p);
+    pv<D, SLOT * Shape<D>::SLOT>(o, p, fr);
+  }
+};
+
+template <int D, int NBUF>
+__global__ void __launch_bounds__(128) sparse_kernel(AttnArgs a, XcdGrid grid) {
+  constexpr int NT = Shape<D>::NT;
+  static_assert(NBUF >= 2 && NBUF <= 3, "ring depth");
+  __shared__ __attribute__((aligned(1024))) char ring[NBUF * Shape<D>::SLOT];
   __shared__ int seq[kMaxBlocks];
-  __shared__ unsigned char flags[kMaxBlocks];
 
   const uint32_t lin = grid.linear(blockIdx.x);
   if (lin >= grid.total) return;
   const int Nb = a.Nb, N = a.N, keep = a.keep;
   const int bh = lin / Nb, qi = lin % Nb;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const size_t head = (size_t)bh * N * D;
-  const char* qbase = (const char*)a.q + head * 2;
-  const char* kbase = (const char*)a.k + head * 2;
-  const char* vbase = (const char*)a.v + head * 2;
   const int32_t* list = a.idx + ((size_t)bh * Nb + qi) * keep;
-
-  // Processing order: the kept list, then (calibration only) every other block ascending.
-  const int nseq = MODE == AttnMode::kCalibrate ? Nb : keep;
-  for (int n = threadIdx.x; n < keep; n += kThreads) seq[n] = min(max(list[n], 0), Nb - 1);
-  if (MODE == AttnMode::kCalibrate) {
-    for (int n = threadIdx.x; n < Nb; n += kThreads) flags[n] = 0;
-    __syncthreads();
-    for (int n = threadIdx.x; n < keep; n += kThreads) flags[seq[n]] = 1;
-    __syncthreads();
-    if (wave == 0) {
-      int cnt = keep;
-      for (int base = 0; base < Nb; base += 64) {
-        int j = base + lane;
-        bool f = j < Nb && !flags[j];
-        unsigned long long mk = __ballot(f);
-        const int pos = cnt + __popcll(mk & ((1ull << lane) - 1ull));
-        if (f && pos < kMaxBlocks) seq[pos] = j;  // bounded even for a list with repeats
-        cnt += __popcll(mk);
-      }
-    }
-    if (a.idx_cache != nullptr) {
-      int32_t* dst = a.idx_cache + ((size_t)bh * Nb + qi) * keep;
-      for (int n = threadIdx.x; n < keep; n += kThreads) dst[n] = list[n];
-    }
-  }
-  // Zero the padding units of the V rows: the last O^T tile of D = 80 reads
-  // them as channels 80..95 (those output rows are discarded; zeros keep them finite).
-  if (Shape<D>::RSU > Shape<D>::UNITS) {
-    for (int r = threadIdx.x; r < kBlock; r += kThreads)
-      for (int u = Shape<D>::UNITS; u < Shape<D>::RSU; ++u) *(u32x4*)(lds_v + lds_off<D>(r, u)) = u32x4{};
-  }
-  __syncthreads();
-
-  // Q^T operand for this wave's 32 rows (rows >= N read as zero).
-  WaveState<D> st;
   const int row = qi * kBlock + wave * 32 + l32;
   const bool row_ok = row < N;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4 raw = u32x4{};
-    if (row_ok) raw = *(const u32x4*)(qbase + ((size_t)row * D + 16 * ks + 8 * g) * 2);
-    st.q[ks] = __builtin_bit_cast(bf16x8, raw);
-  }
-#pragma unroll
-  for (int t = 0; t < NT; ++t) st.o[t] = f32x16{};
-  st.m_raw = -INFINITY;
-  st.z = 0.f;
-  const float c = a.alpha * kLog2e;
+  const size_t srow = (size_t)bh * N + (row_ok ? row : N - 1);
 
-  f32x16 okept[MODE == AttnMode::kCalibrate ? NT : 1];
-  float m_kept = 0.f, z_kept = 0.f;
+  // Memory order: the list and Q (both needed first), then the first tiles,
+  // then the statistics and the residual (needed last).
+  SparseCtx<D, NBUF> cx;
+  for (int n = threadIdx.x; n < keep; n += 128) seq[n] = min(max(list[n], 0), Nb - 1);
+  load_q<D>(cx.st, (const char*)a.q + head * 2, row, N);
+  cx.ring = ring;
+  cx.seq = seq;
+  cx.kbase = (const char*)a.k + head * 2;
+  cx.vbase = (const char*)a.v + head * 2;
+  cx.keep = keep;
+  cx.N = N;
+  cx.c = a.alpha * kLog2e;
+  cx.dma.init(wave, lane);
+  cx.fr.init(ring);
+  __syncthreads();  // list and Q in place
 
-  Tile<D> tile;
-  int cur = __builtin_amdgcn_readfirstlane(seq[0]);
-  load_tile<D>(tile, kbase, vbase, cur, N);
-  for (int n = 0; n < nseq; ++n) {
-    __syncthreads();
-    store_tile<D>(tile, lds_k, lds_v);
-    __syncthreads();
-    int nxt = cur;
-    if (n + 1 < nseq) {
-      nxt = __builtin_amdgcn_readfirstlane(seq[n + 1]);
-      load_tile<D>(tile, kbase, vbase, nxt, N);
-    }
-    if (MODE == AttnMode::kCalibrate && n == keep) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) { okept[t] = st.o[t]; st.o[t] = f32x16{}; }
-      m_kept = st.m_raw;
-      z_kept = st.z;
-      st.z = 0.f;
-    }
-    attend_block<D>(st, lds_k, lds_v, min(kBlock, N - cur * kBlock), c);
-    cur = nxt;
-  }
+  for (int t = 0; t < NBUF - 1; ++t)
+    if (t < keep)
+      cx.dma.issue(ring + t * Shape<D>::SLOT, cx.kbase, cx.vbase, __builtin_amdgcn_readfirstlane(seq[t]), N);
 
-  // Epilogue.  Every lane holds 16 * NT output values of row `row`:
-  // d = 32t + 8(i/4) + 4g + (i%4).
-  const size_t srow = (size_t)bh * N + row;
-  if (MODE == AttnMode::kCalibrate) {
-    if (nseq == keep) {  // nothing masked: everything so far is the kept part
+  const float m_c = a.m[srow], zf_c = a.z_full[srow], zs_c = a.z_sparse[srow];
+  f32x4 rc[NT][4];
+  {
+    const float* rrow = a.R + srow * D;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) { okept[t] = st.o[t]; st.o[t] = f32x16{}; }
-      m_kept = st.m_raw;
-      z_kept = st.z;
-      st.z = 0.f;
-    }
-    const float corr = __builtin_amdgcn_exp2f((m_kept - st.m_raw) * c);
-    float zs = z_kept * corr;
-    zs += xor32(zs);
-    float zm = st.z + xor32(st.z);
-    const float zf = zs + zm;
-    const float inv = 1.f / zf;
-    if (row_ok) {
-      if (g == 0) {
-        a.m[srow] = st.m_raw * a.alpha;
-        a.z_full[srow] = zf;
-        a.z_sparse[srow] = zs;
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * t + 8 * i4 + 4 * g;
+        rc[t][i4] = d < D ? __builtin_nontemporal_load((const f32x4*)(rrow + d)) : f32x4{};
       }
-      float* rrow = a.R + srow * D;
-      __bf16* orow = (__bf16*)a.o + srow * D;
+  }
+
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+  for (int t = 0; t < NT; ++t) cx.o[t] = f32x16{};
+  cx.z = 0.f;
+  for (int n = 0; n < keep; n += NBUF) {
+    cx.template step<0>(n);
+    if (n + 1 < keep) cx.template step<1>(n + 1);
+    if constexpr (NBUF > 2)
+      if (n + 2 < keep) cx.template step<2>(n + 2);
+  }
+
+  // O = (N e^{m-M} + R_c e^{m_c-M}) / (Z e^{m-M} Z_full_c / Z_sparse_c), M = max(m, m_c);
+  // N and Z are relative to m = the reference max (any reference gives the same O).
+  const float z = pair_sum(cx.z);
+  if (row_ok) {
+    const float m_cur = cx.st.m_ref * a.alpha;
+    const float big = fmaxf(m_cur, m_c);
+    const float e1 = expf(m_cur - big), e2 = expf(m_c - big);
+    const float inv = 1.f / (z * e1 * zf_c / zs_c);
+    const float w1 = e1 * inv, w2 = e2 * inv;
+    __bf16* orow = (__bf16*)a.o + srow * D;
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          int d = 32 * t + 8 * i4 + 4 * g;
-          if (d < D) {
-            f32x4 r, o;
-            __bf16 ob[4];
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              r[e] = st.o[t][4 * i4 + e];
-              o[e] = (okept[t][4 * i4 + e] * corr + r[e]) * inv;
-              ob[e] = (__bf16)o[e];
-            }
-            *(f32x4*)(rrow + d) = r;
-            *(u32x2*)(orow + d) = *(u32x2*)ob;
-          }
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * t + 8 * i4 + 4 * g;
+        if (d < D) {
+          __bf16 ob[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ob[e] = (__bf16)(cx.o[t][4 * i4 + e] * w1 + rc[t][i4][e] * w2);
+          *(u32x2*)(orow + d) = *(u32x2*)ob;
         }
-    }
-  } else {
-    float z = st.z + xor32(st.z);
-    if (row_ok) {
-      const float m_cur = st.m_raw * a.alpha;
-      const float m_c = a.m[srow];
-      const float zf_c = a.z_full[srow], zs_c = a.z_sparse[srow];
-      const float big = fmaxf(m_cur, m_c);
-      const float e1 = expf(m_cur - big), e2 = expf(m_c - big);
-      const float inv = 1.f / (z * e1 * zf_c / zs_c);
-      const float w1 = e1 * inv, w2 = e2 * inv;
-      const float* rrow = a.R + srow * D;
-      __bf16* orow = (__bf16*)a.o + srow * D;
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          int d = 32 * t + 8 * i4 + 4 * g;
-          if (d < D) {
-            f32x4 r = *(const f32x4*)(rrow + d);
-            __bf16 ob[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ob[e] = (__bf16)(st.o[t][4 * i4 + e] * w1 + r[e] * w2);
-            *(u32x2*)(orow + d) = *(u32x2*)ob;
-          }
-        }
-    }
+      }
   }
 }
 
-template <int D, AttnMode MODE>
-hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
-  XcdGrid grid = make_xcd_grid((uint32_t)a.BH * (uint32_t)a.Nb);
-  hipLaunchKernelGGL((attn_bf16_kernel<D, MODE>), dim3(grid.grid()), dim3(kThreads), 0, s, a, grid);
+// ---------------------------------------------------------------- calibration step
+template <int D, int NBUF, int QB>
+struct CalibCtx {
+  static constexpr int NT = Shape<D>::NT;
+  using Dma = TileDma<D, 2 * QB>;
+  char* ring;
+  const unsigned char* flags;  // this wave's query block: 1 = kept key block
+  const char* kbase;
+  const char* vbase;
+  int Nb, N;
+  bool active;
+  float c;
+  Dma dma;
+  Frag<D> fr;
+  Rows<D> st;
+  f32x16 okept[NT], ores[NT];
+  float zk, zm;
+
+  template <int SLOT>
+  __device__ __forceinline__ void step(int j) {
+    wait_tile<Dma::IPT>(min(NBUF - 2, Nb - 1 - j));
+    __builtin_amdgcn_s_barrier();
+    if (j + NBUF - 1 < Nb) {
+      constexpr int NEXT = (SLOT + NBUF - 1) % NBUF;
+      dma.issue(ring + NEXT * Shape<D>::SLOT, kbase, vbase, j + NBUF - 1, N);
+    }
+    if (!active) return;
+    const bool kept = __builtin_amdgcn_readfirstlane(flags[j]) != 0;
+    f32x16 s[2];
+    scores<D, SLOT * Shape<D>::SLOT>(s, st, fr, min(kBlock, N - j * kBlock));
+    bool any;
+    const float corr = update_max(st.m_ref, st.m_true, row_max(s), c, &any);
+    if (any) {
+      zk *= corr;
+      zm *= corr;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        okept[t] *= corr;
+        ores[t] *= corr;
+      }
+    }
+    bf16x8 p[2][2];
+    const float zb = probs(p, s, st.m_ref, c);
+    if (kept) {
+      zk += zb;
+      pv<D, SLOT * Shape<D>::SLOT>(okept, p, fr);
+    } else {
+      zm += zb;
+      pv<D, SLOT * Shape<D>::SLOT>(ores, p, fr);
+    }
+  }
+};
+
+template <int D, int NBUF, int QB>
+__global__ void __launch_bounds__(128 * QB) calib_kernel(AttnArgs a, XcdGrid grid) {
+  constexpr int NT = Shape<D>::NT;
+  static_assert(NBUF >= 2 && NBUF <= 3, "ring depth");
+  __shared__ __attribute__((aligned(1024))) char ring[NBUF * Shape<D>::SLOT];
+  __shared__ unsigned char flags[QB][kMaxBlocks];
+
+  const uint32_t lin = grid.linear(blockIdx.x);
+  if (lin >= grid.total) return;
+  const int Nb = a.Nb, N = a.N, keep = a.keep;
+  const int groups = (Nb + QB - 1) / QB;
+  const int bh = lin / groups, q0 = (lin % groups) * QB;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int qb = wave >> 1, qi = q0 + qb;
+  const size_t head = (size_t)bh * N * D;
+
+  for (int n = threadIdx.x; n < QB * kMaxBlocks; n += 128 * QB) (&flags[0][0])[n] = 0;
+  __syncthreads();
+  for (int e = threadIdx.x; e < QB * keep; e += 128 * QB) {
+    const int b = e / keep, n = e % keep;
+    if (q0 + b < Nb) {
+      const size_t at = ((size_t)bh * Nb + q0 + b) * keep + n;
+      const int j = a.idx[at];
+      flags[b][min(max(j, 0), Nb - 1)] = 1;
+      if (a.idx_cache != nullptr) a.idx_cache[at] = j;
+    }
+  }
+
+  CalibCtx<D, NBUF, QB> cx;
+  const int row = qi * kBlock + (wave & 1) * 32 + l32;
+  const bool row_ok = qi < Nb && row < N;
+  load_q<D>(cx.st, (const char*)a.q + head * 2, qi < Nb ? row : N, N);
+  cx.ring = ring;
+  cx.flags = flags[qb];
+  cx.kbase = (const char*)a.k + head * 2;
+  cx.vbase = (const char*)a.v + head * 2;
+  cx.Nb = Nb;
+  cx.N = N;
+  cx.active = qi < Nb;
+  cx.c = a.alpha * kLog2e;
+  cx.dma.init(wave, lane);
+  cx.fr.init(ring);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) cx.okept[t] = cx.ores[t] = f32x16{};
+  cx.zk = cx.zm = 0.f;
+  __syncthreads();  // flags and Q in place
+
+#pragma unroll
+  for (int t = 0; t < NBUF - 1; ++t)
+    if (t < Nb) cx.dma.issue(ring + t * Shape<D>::SLOT, cx.kbase, cx.vbase, t, N);
+
+  for (int j = 0; j < Nb; j += NBUF) {
+    cx.template step<0>(j);
+    if (j + 1 < Nb) cx.template step<1>(j + 1);
+    if constexpr (NBUF > 2)
+      if (j + 2 < Nb) cx.template step<2>(j + 2);
+  }
+
+  // Statistics relative to the true row max m: factor e^{m_ref - m}.
+  const float f = __builtin_amdgcn_exp2f((cx.st.m_ref - cx.st.m_true) * cx.c);
+  const float zs = pair_sum(cx.zk) * f;
+  const float zf = zs + pair_sum(cx.zm) * f;
+  if (row_ok) {
+    const size_t srow = (size_t)bh * N + row;
+    if (g == 0) {
+      a.m[srow] = cx.st.m_true * a.alpha;
+      a.z_full[srow] = zf;
+      a.z_sparse[srow] = zs;
+    }
+    const float inv = 1.f / zf;
+    float* rrow = a.R + srow * D;
+    __bf16* orow = (__bf16*)a.o + srow * D;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * t + 8 * i4 + 4 * g;
+        if (d < D) {
+          f32x4 r;
+          __bf16 ob[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            r[e] = cx.ores[t][4 * i4 + e] * f;
+            ob[e] = (__bf16)((cx.okept[t][4 * i4 + e] * f + r[e]) * inv);
+          }
+          *(f32x4*)(rrow + d) = r;
+          *(u32x2*)(orow + d) = *(u32x2*)ob;
+        }
+      }
+  }
+}
+
+constexpr int kSparseRing = 2;
+constexpr int kCalibRing = 3;
+
+template <int D>
+hipError_t launch_d(AttnMode mode, const AttnArgs& a, hipStream_t s) {
+  if (mode == AttnMode::kSparse) {
+    XcdGrid grid = make_xcd_grid((uint32_t)a.BH * (uint32_t)a.Nb);
+    hipLaunchKernelGGL((sparse_kernel<D, kSparseRing>), dim3(grid.grid()), dim3(128), 0, s, a, grid);
+  } else {
+    constexpr int QB = D == 64 ? 4 : 2;  // 2*QB waves must divide the LDS row units
+    const uint32_t groups = (uint32_t)(a.Nb + QB - 1) / QB;
+    XcdGrid grid = make_xcd_grid((uint32_t)a.BH * groups);
+    hipLaunchKernelGGL((calib_kernel<D, kCalibRing, QB>), dim3(grid.grid()), dim3(128 * QB), 0, s, a, grid);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_bf16(AttnMode mode, int D, const AttnArgs& a, hipStream_t s) {
-  if (D == 64) return mode == AttnMode::kCalibrate ? launch_one<64, AttnMode::kCalibrate>(a, s)
-                                                   : launch_one<64, AttnMode::kSparse>(a, s);
-  if (D == 80) return mode == AttnMode::kCalibrate ? launch_one<80, AttnMode::kCalibrate>(a, s)
-                                                   : launch_one<80, AttnMode::kSparse>(a, s);
+  if (D == 64) return launch_d<64>(mode, a, s);
+  if (D == 80) return launch_d<80>(mode, a, s);
   return hipErrorInvalidValue;
 }
 

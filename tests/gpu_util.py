@@ -23,6 +23,7 @@ def errors(got, ref):
 def assert_close(got, ref, max_rel=MAX_REL, l1_rel=L1_REL, what="O"):
     assert np.all(np.isfinite(np.asarray(got, dtype=np.float64))), f"{what}: non-finite values"
     mx, l1 = errors(got, ref)
+    print(f"[err] {what}: max-rel {mx:.3e} L1-rel {l1:.3e}", flush=True)
     assert mx <= max_rel and l1 <= l1_rel, f"{what}: max-rel {mx:.3e} (<= {max_rel}), L1-rel {l1:.3e} (<= {l1_rel})"
     return mx, l1
 

@@ -369,13 +369,11 @@ def test_cogvideox5b_layers_and_recalibration():
         cal_inputs = None
         for s in range(12):
             q, k, v = (synth.store(x, cfg["dtype"]) for x in it.next())
-            if s < 9:
-                continue
             o = gu.empty_out(sh)
             did = rettn.rt_attention_step(sh, q, k, v, forced, cache, layer, s, cfg["period"], o, ws)
             torch.cuda.synchronize()
-            assert did == (s == 10)
-            if s == 9:
+            assert did == (s in (0, 10))
+            if s < 10:
                 continue
             if s == 10:
                 cal_inputs = {bh: [gu.host(x[bh[0], bh[1]]) for x in (q, k, v)] for bh in heads}
