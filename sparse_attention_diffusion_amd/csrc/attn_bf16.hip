@@ -261,12 +261,13 @@ __device__ __forceinline__ void scores(f32x16 (&s)[2], const Rows<D>& st, const 
 }
 
 __device__ __forceinline__ float row_max(const f32x16 (&s)[2]) {
-  float mx = -INFINITY;
+  float m0 = -INFINITY, m1 = -INFINITY;  // two independent chains
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
-  return pair_max(mx);
+  for (int i = 0; i < 16; ++i) {
+    m0 = fmaxf(m0, s[0][i]);
+    m1 = fmaxf(m1, s[1][i]);
+  }
+  return pair_max(fmaxf(m0, m1));
 }
 
 // Raises the reference max when some row of the wave needs it; returns the
@@ -336,19 +337,16 @@ __device__ __forceinline__ void pv(f32x16 (&o)[Shape<D>::NT], const bf16x8 (&p)[
   }
 }
 
-// Q^T operand of this lane's row; rows >= N read row N-1 and are zeroed
-// (every lane issues the same loads).
+// Q^T operand of this lane's row.  Rows >= N read row N-1 instead (every lane
+// issues the same loads); their results are never stored.
 template <int D>
 __device__ __forceinline__ void load_q(Rows<D>& st, const char* qbase, int row, int N) {
   const int g = (threadIdx.x & 63) >> 5;
-  const bool ok = row < N;
-  const size_t r = (size_t)(ok ? row : N - 1);
+  const size_t r = (size_t)min(row, N - 1);
 #pragma unroll
-  for (int ks = 0; ks < Shape<D>::KS; ++ks) {
-    u32x4 raw = __builtin_nontemporal_load((const u32x4*)(qbase + (r * D + 16 * ks + 8 * g) * 2));
-    if (!ok) raw = u32x4{};
-    st.q[ks] = __builtin_bit_cast(bf16x8, raw);
-  }
+  for (int ks = 0; ks < Shape<D>::KS; ++ks)
+    st.q[ks] = __builtin_bit_cast(
+        bf16x8, __builtin_nontemporal_load((const u32x4*)(qbase + (r * D + 16 * ks + 8 * g) * 2)));
   st.m_ref = -INFINITY;
   st.m_true = -INFINITY;
 }
@@ -359,12 +357,14 @@ struct SparseCtx {
   static constexpr int NT = Shape<D>::NT;
   using Dma = TileDma<D, 2>;
   char* ring;
-  const int* seq;
+  const __attribute__((address_space(4))) int32_t* list;  // kept blocks, read with scalar loads
   const char* kbase;
   const char* vbase;
-  int keep, N;
+  int keep, N, Nb;
   float c;
   Dma dma;
+
+  __device__ __forceinline__ int block_at(int n) const { return min(max(list[n], 0), Nb - 1); }
   Frag<D> fr;
   Rows<D> st;
   f32x16 o[NT];
@@ -377,9 +377,9 @@ struct SparseCtx {
     __builtin_amdgcn_s_barrier();
     if (n + NBUF - 1 < keep) {
       constexpr int NEXT = (SLOT + NBUF - 1) % NBUF;
-      dma.issue(ring + NEXT * Shape<D>::SLOT, kbase, vbase, __builtin_amdgcn_readfirstlane(seq[n + NBUF - 1]), N);
+      dma.issue(ring + NEXT * Shape<D>::SLOT, kbase, vbase, block_at(n + NBUF - 1), N);
     }
-    const int j = __builtin_amdgcn_readfirstlane(seq[n]);
+    const int j = block_at(n);
     f32x16 s[2];
     scores<D, SLOT * Shape<D>::SLOT>(s, st, fr, min(kBlock, N - j * kBlock));
     bool any;
@@ -401,7 +401,6 @@ __global__ void __launch_bounds__(128) sparse_kernel(AttnArgs a, XcdGrid grid) {
   constexpr int NT = Shape<D>::NT;
   static_assert(NBUF >= 2 && NBUF <= 3, "ring depth");
   __shared__ __attribute__((aligned(1024))) char ring[NBUF * Shape<D>::SLOT];
-  __shared__ int seq[kMaxBlocks];
 
   const uint32_t lin = grid.linear(blockIdx.x);
   if (lin >= grid.total) return;
@@ -411,31 +410,27 @@ __global__ void __launch_bounds__(128) sparse_kernel(AttnArgs a, XcdGrid grid) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const size_t head = (size_t)bh * N * D;
-  const int32_t* list = a.idx + ((size_t)bh * Nb + qi) * keep;
   const int row = qi * kBlock + wave * 32 + l32;
   const bool row_ok = row < N;
   const size_t srow = (size_t)bh * N + (row_ok ? row : N - 1);
 
-  // Memory order: the list and Q (both needed first), then the first tiles,
-  // then the statistics and the residual (needed last).
+  // Memory order: the first tiles (their block indices come from scalar loads
+  // of the list), then Q, then the statistics and the residual (needed last).
   SparseCtx<D, NBUF> cx;
-  for (int n = threadIdx.x; n < keep; n += 128) seq[n] = min(max(list[n], 0), Nb - 1);
-  load_q<D>(cx.st, (const char*)a.q + head * 2, row, N);
   cx.ring = ring;
-  cx.seq = seq;
+  cx.list = (const __attribute__((address_space(4))) int32_t*)(a.idx + ((size_t)bh * Nb + qi) * keep);
   cx.kbase = (const char*)a.k + head * 2;
   cx.vbase = (const char*)a.v + head * 2;
   cx.keep = keep;
   cx.N = N;
+  cx.Nb = Nb;
   cx.c = a.alpha * kLog2e;
   cx.dma.init(wave, lane);
   cx.fr.init(ring);
-  __syncthreads();  // list and Q in place
-
 #pragma unroll
   for (int t = 0; t < NBUF - 1; ++t)
-    if (t < keep)
-      cx.dma.issue(ring + t * Shape<D>::SLOT, cx.kbase, cx.vbase, __builtin_amdgcn_readfirstlane(seq[t]), N);
+    if (t < keep) cx.dma.issue(ring + t * Shape<D>::SLOT, cx.kbase, cx.vbase, cx.block_at(t), N);
+  load_q<D>(cx.st, (const char*)a.q + head * 2, row, N);
 
   const float m_c = a.m[srow], zf_c = a.z_full[srow], zs_c = a.z_sparse[srow];
   f32x4 rc[NT][4];

@@ -1,0 +1,121 @@
+"""Summarise rocprofv3 CSV output for this library's kernels.
+
+Two kinds of input, both written by rocprofv3 with ``--output-format csv``:
+
+* a kernel trace (``--kernel-trace --stats``): per-kernel call counts and
+  average durations;
+* counter runs (``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``) over a run of
+  ``bench.py --traffic-probe``, which first copies 512 MiB with a plain copy
+  kernel.  The counters read for that copy against its known size give the
+  scale factors that turn the sparse kernel's counters into HBM bytes.
+
+Usage:
+  python -m sparse_attention_diffusion_amd.profsum --trace DIR [--fetch DIR --write DIR]
+         --config cogvideox2b --command "..." --out profiles/
+"""
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SRC = os.path.join(HERE, "csrc", "attn_bf16.hip")
+COPY_BYTES = 512 << 20
+
+SHORT = [("sparse_kernel<64", "sparse reshape (d_pad 64)"), ("sparse_kernel<80", "sparse reshape (d_pad 80)"),
+         ("calib_kernel<64", "calibration (d_pad 64)"), ("calib_kernel<80", "calibration (d_pad 80)"),
+         ("attn_f32_kernel", "float32 attention"), ("select_kernel", "block top-k"), ("pool_kernel", "block pooling")]
+
+
+def short_name(name):
+    for key, label in SHORT:
+        if key in name:
+            return label
+    return None
+
+
+def source_hash():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def _one(pattern):
+    hits = sorted(glob.glob(pattern, recursive=True))
+    if not hits:
+        raise FileNotFoundError(pattern)
+    return hits[0]
+
+
+def trace_stats(d):
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*kernel_stats.csv")))))
+    out = []
+    for r in rows:
+        label = short_name(r["Name"])
+        if label:
+            out.append(dict(kernel=label, name=r["Name"][:120], calls=int(r["Calls"]),
+                            avg_us=float(r["AverageNs"]) / 1e3, min_us=float(r["MinNs"]) / 1e3,
+                            max_us=float(r["MaxNs"]) / 1e3, total_ms=float(r["TotalDurationNs"]) / 1e6))
+    return out
+
+
+def counters(d, counter):
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*counter_collection.csv")))))
+    copy = [float(r["Counter_Value"]) for r in rows
+            if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]]
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        label = short_name(r["Kernel_Name"])
+        if label:
+            per.setdefault(label, []).append(float(r["Counter_Value"]))
+    if not copy:
+        raise RuntimeError("no copy probe dispatch in " + d)
+    scale = COPY_BYTES / (max(copy) * 1024.0)  # counters are in KiB
+    return scale, {k: sum(v) / len(v) * 1024.0 * scale for k, v in per.items()}, max(copy)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--config", default="cogvideox2b")
+    ap.add_argument("--command", required=True, help="the command line that produced the trace")
+    ap.add_argument("--pmc-command", default="")
+    ap.add_argument("--out", required=True)
+    args = ap.parse_args()
+    os.makedirs(args.out, exist_ok=True)
+    stats = trace_stats(args.trace)
+    lines = [f"# rocprofv3 kernel trace: {args.config}", "", "Command:", "", "    " + args.command, "",
+             "| kernel | calls | avg us | min us | max us | total ms |", "|---|---|---|---|---|---|"]
+    for s in sorted(stats, key=lambda x: -x["total_ms"]):
+        lines.append(f"| {s['kernel']} | {s['calls']} | {s['avg_us']:.2f} | {s['min_us']:.2f} | {s['max_us']:.2f} "
+                     f"| {s['total_ms']:.3f} |")
+    lines += ["", f"Kernel source sha256[:16] of attn_bf16.hip: {source_hash()}"]
+    if args.fetch and args.write:
+        fs, fetch, fraw = counters(args.fetch, "FETCH_SIZE")
+        ws, write, wraw = counters(args.write, "WRITE_SIZE")
+        lines += ["", "## HBM traffic per launch (rocprofv3 --pmc, scaled by a 512 MiB copy probe)", "",
+                  "Command (one run per counter):", "", "    " + args.pmc_command, "",
+                  f"Copy probe: FETCH_SIZE read {fraw:.0f} KiB and WRITE_SIZE {wraw:.0f} KiB for {COPY_BYTES >> 10} KiB "
+                  f"moved; scale factors {fs:.3f} (fetch) and {ws:.3f} (write).", "",
+                  "| kernel | fetch MB | write MB | total MB |", "|---|---|---|---|"]
+        for k in sorted(set(fetch) | set(write)):
+            f, w = fetch.get(k, 0.0), write.get(k, 0.0)
+            lines.append(f"| {k} | {f / 1e6:.1f} | {w / 1e6:.1f} | {(f + w) / 1e6:.1f} |")
+        label = "sparse reshape (d_pad 64)"
+        if label in fetch and label in write:
+            rec = dict(config=args.config, kernel=label, kernel_source_sha256_16=source_hash(),
+                       fetch_bytes=fetch[label], write_bytes=write[label],
+                       bytes_per_launch=fetch[label] + write[label], fetch_scale=fs, write_scale=ws,
+                       command=args.pmc_command)
+            json.dump(rec, open(os.path.join(args.out, f"sparse_attn_reshape_{args.config}_traffic.json"), "w"),
+                      indent=1)
+    open(os.path.join(args.out, f"kernels_{args.config}.md"), "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()
