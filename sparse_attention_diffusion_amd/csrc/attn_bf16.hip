@@ -123,15 +123,24 @@ struct TileDma {
   // past N read row N-1 (finite data; their scores are masked).
   __device__ __forceinline__ void issue(char* slot, const char* kbase, const char* vbase, int j, int N) const {
     const size_t blk = (size_t)j * kBlock * D * 2;
+    const char* kb = kbase + blk;
+    const char* vb = vbase + blk;
     const int nvalid = N - j * kBlock;
+    if (nvalid >= kBlock) {  // uniform: every block but a short last one
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      uint32_t o = off[i];
-      if (nvalid < kBlock) o -= (uint32_t)(max(0, row[i] - (nvalid - 1)) * D * 2);
-      char* dst = slot + (wave + W * i) * 1024;
-      __builtin_amdgcn_global_load_lds((const void*)(kbase + blk + o), (lds_void*)dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vbase + blk + o), (lds_void*)(dst + Shape<D>::TILE), 16, 0,
-                                       0);
+      for (int i = 0; i < NI; ++i) {
+        char* dst = slot + (wave + W * i) * 1024;
+        __builtin_amdgcn_global_load_lds((const void*)(kb + off[i]), (lds_void*)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vb + off[i]), (lds_void*)(dst + Shape<D>::TILE), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const uint32_t o = off[i] - (uint32_t)(max(0, row[i] - (nvalid - 1)) * D * 2);
+        char* dst = slot + (wave + W * i) * 1024;
+        __builtin_amdgcn_global_load_lds((const void*)(kb + o), (lds_void*)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vb + o), (lds_void*)(dst + Shape<D>::TILE), 16, 0, 0);
+      }
     }
   }
 };
@@ -163,31 +172,42 @@ struct Frag {
   }
 };
 
-// K operands of one 32-key half: KS ds_read_b128, waited for in the same statement.
-template <int KS, int OFF>
-__device__ __forceinline__ void k_reads(u32x4 (&a)[KS], const uint32_t (&ad)[KS]) {
-  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+// K operands of one key block, both 32-key halves (offset OFF and OFF + H):
+// 2*KS ds_read_b128 waited for in the same statement.  a[t*KS + ks].
+template <int KS, int OFF, int H>
+__device__ __forceinline__ void k_reads(u32x4 (&a)[2 * KS], const uint32_t (&ad)[KS]) {
+  static_assert(OFF >= 0 && OFF + H < 65536, "ds offset");
   if constexpr (KS == 4) {
     asm volatile(
-        "ds_read_b128 %0, %4 offset:%8\n\t"
-        "ds_read_b128 %1, %5 offset:%8\n\t"
-        "ds_read_b128 %2, %6 offset:%8\n\t"
-        "ds_read_b128 %3, %7 offset:%8\n\t"
+        "ds_read_b128 %0, %8 offset:%12\n\t"
+        "ds_read_b128 %1, %9 offset:%12\n\t"
+        "ds_read_b128 %2, %10 offset:%12\n\t"
+        "ds_read_b128 %3, %11 offset:%12\n\t"
+        "ds_read_b128 %4, %8 offset:%13\n\t"
+        "ds_read_b128 %5, %9 offset:%13\n\t"
+        "ds_read_b128 %6, %10 offset:%13\n\t"
+        "ds_read_b128 %7, %11 offset:%13\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
-        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "i"(OFF)
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "i"(OFF), "i"(OFF + H)
         : "memory");
   } else {
     static_assert(KS == 5, "k-steps");
     asm volatile(
-        "ds_read_b128 %0, %5 offset:%10\n\t"
-        "ds_read_b128 %1, %6 offset:%10\n\t"
-        "ds_read_b128 %2, %7 offset:%10\n\t"
-        "ds_read_b128 %3, %8 offset:%10\n\t"
-        "ds_read_b128 %4, %9 offset:%10\n\t"
+        "ds_read_b128 %0, %10 offset:%15\n\t"
+        "ds_read_b128 %1, %11 offset:%15\n\t"
+        "ds_read_b128 %2, %12 offset:%15\n\t"
+        "ds_read_b128 %3, %13 offset:%15\n\t"
+        "ds_read_b128 %4, %14 offset:%15\n\t"
+        "ds_read_b128 %5, %10 offset:%16\n\t"
+        "ds_read_b128 %6, %11 offset:%16\n\t"
+        "ds_read_b128 %7, %12 offset:%16\n\t"
+        "ds_read_b128 %8, %13 offset:%16\n\t"
+        "ds_read_b128 %9, %14 offset:%16\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4])
-        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "i"(OFF)
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7]),
+          "=&v"(a[8]), "=&v"(a[9])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "i"(OFF), "i"(OFF + H)
         : "memory");
   }
 }
@@ -232,22 +252,21 @@ struct Rows {
 
 // S^T = K Q^T for the key block in the slot at byte offset SLOT_OFF; keys at
 // or past nvalid are set to -inf.  s[t][i] is key 32t + 8(i/4) + 4g + i%4.
-template <int D, int OFF>
-__device__ __forceinline__ f32x16 scores_half(const Rows<D>& st, const Frag<D>& fr) {
-  constexpr int KS = Shape<D>::KS;
-  u32x4 a[KS];
-  k_reads<KS, OFF>(a, fr.k);
-  f32x16 s = {};
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[ks]), st.q[ks], s, 0, 0, 0);
-  return s;
-}
-
+// S^T = K Q^T for the key block in the slot at byte offset SLOT_OFF; keys at
+// or past nvalid are set to -inf.  s[t][i] is key 32t + 8(i/4) + 4g + i%4.
+// The two 32-key halves are independent MFMA chains, issued alternately.
 template <int D, int SLOT_OFF>
 __device__ __forceinline__ void scores(f32x16 (&s)[2], const Rows<D>& st, const Frag<D>& fr, int nvalid) {
-  s[0] = scores_half<D, SLOT_OFF>(st, fr);
-  s[1] = scores_half<D, SLOT_OFF + 32 * Shape<D>::ROW>(st, fr);
+  constexpr int KS = Shape<D>::KS;
+  u32x4 a[2 * KS];
+  k_reads<KS, SLOT_OFF, 32 * Shape<D>::ROW>(a, fr.k);
+  s[0] = f32x16{};
+  s[1] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[ks]), st.q[ks], s[0], 0, 0, 0);
+    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[KS + ks]), st.q[ks], s[1], 0, 0, 0);
+  }
   if (nvalid < kBlock) {
     const int g = (threadIdx.x & 63) >> 5;
 #pragma unroll
@@ -317,24 +336,38 @@ __device__ __forceinline__ float sum_rounded(const bf16x8 (&p)[2][2]) {
   return z0 + z1;
 }
 
-// O^T += V^T P^T for the key block in the slot at SLOT_OFF.  k-step (t, hs)
-// covers keys 32t + 16hs + 0..15; lane group g holds slots j <-> key
-// 32t + 16hs + 8(j/4) + 4g + j%4 in both operands.
+// V^T operands of the key block in the slot at SLOT_OFF, all d tiles:
+// h[dt][t][hs][hh].  Fetched before the softmax so that the LDS latency
+// overlaps the exponentials.
 template <int D, int SLOT_OFF>
-__device__ __forceinline__ void pv(f32x16 (&o)[Shape<D>::NT], const bf16x8 (&p)[2][2], const Frag<D>& fr) {
+__device__ __forceinline__ void v_fetch(u32x2 (&h)[Shape<D>::NT][2][2][2], const Frag<D>& fr) {
   constexpr int ROW = Shape<D>::ROW;
 #pragma unroll
-  for (int dt = 0; dt < Shape<D>::NT; ++dt) {
-    u32x2 h[2][2][2];
-    tr_reads<SLOT_OFF, 32 * ROW, 16 * ROW>(h, fr.v[dt][0], fr.v[dt][1]);
+  for (int dt = 0; dt < Shape<D>::NT; ++dt) tr_reads<SLOT_OFF, 32 * ROW, 16 * ROW>(h[dt], fr.v[dt][0], fr.v[dt][1]);
+}
+
+// O^T += V^T P^T.  k-step (t, hs) covers keys 32t + 16hs + 0..15; lane group g
+// holds slots j <-> key 32t + 16hs + 8(j/4) + 4g + j%4 in both operands.  The
+// d tiles are independent MFMA chains, issued alternately.
+template <int D>
+__device__ __forceinline__ void pv_mfma(f32x16 (&o)[Shape<D>::NT], const bf16x8 (&p)[2][2],
+                                        const u32x2 (&h)[Shape<D>::NT][2][2][2]) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        const u32x4 both = __builtin_shufflevector(h[t][hs][0], h[t][hs][1], 0, 1, 2, 3);
+    for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+      for (int dt = 0; dt < Shape<D>::NT; ++dt) {
+        const u32x4 both = __builtin_shufflevector(h[dt][t][hs][0], h[dt][t][hs][1], 0, 1, 2, 3);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), p[t][hs], o[dt], 0, 0, 0);
       }
-  }
+}
+
+template <int D, int SLOT_OFF>
+__device__ __forceinline__ void pv(f32x16 (&o)[Shape<D>::NT], const bf16x8 (&p)[2][2], const Frag<D>& fr) {
+  u32x2 h[Shape<D>::NT][2][2][2];
+  v_fetch<D, SLOT_OFF>(h, fr);
+  pv_mfma<D>(o, p, h);
 }
 
 // Q^T operand of this lane's row.  Rows >= N read row N-1 instead (every lane
@@ -477,6 +510,204 @@ __global__ void __launch_bounds__(128) sparse_kernel(AttnArgs a, XcdGrid grid) {
           *(u32x2*)(orow + d) = *(u32x2*)ob;
         }
       }
+  }
+}
+
+// ---------------------------------------------------------------- sparse step, persistent
+// A persistent variant of the sparse step: each workgroup walks a strided run
+// of query blocks (all from its XCD's range) and feeds one continuous stream of
+// key-block tiles through the ring, so the next query block's first tiles are
+// already in flight while the current one finishes, and the per-block setup
+// (list, Q, residual) overlaps with compute:
+//   * Q of the next query block is loaded into a second register set one
+//     block ahead;
+//   * the residual and statistics of the current block are loaded right after
+//     its first tile is consumed and waited for at its second tile;
+//   * the block index of every tile comes from scalar loads of the list.
+// Tiles are numbered T = k*keep + n over the workgroup's k-th query block.
+struct PersistGrid {
+  uint32_t total, per, g;  // query blocks, per XCD, workgroups per XCD
+};
+
+// Scalar context of one query block of the persistent walk.
+template <int D>
+struct ItemCtx {
+  const __attribute__((address_space(4))) int32_t* list;  // its kept blocks (scalar loads)
+  const char* kb;                                          // K, V, Q of its head
+  const char* vb;
+  const char* qb;
+  uint32_t lin;
+  int qi, bh;
+  __device__ __forceinline__ void set(const AttnArgs& a, uint32_t l) {
+    lin = l;
+    bh = (int)(l / (uint32_t)a.Nb);
+    qi = (int)(l - (uint32_t)bh * (uint32_t)a.Nb);
+    const size_t head = (size_t)bh * a.N * D * 2;
+    kb = (const char*)a.k + head;
+    vb = (const char*)a.v + head;
+    qb = (const char*)a.q + head;
+    list = (const __attribute__((address_space(4))) int32_t*)(a.idx + (size_t)l * a.keep);
+  }
+  __device__ __forceinline__ int block(int n, int Nb) const { return min(max(list[n], 0), Nb - 1); }
+};
+
+template <int D, int NBUF>
+__global__ void __launch_bounds__(128) sparse_persistent_kernel(AttnArgs a, PersistGrid pg) {
+  constexpr int NT = Shape<D>::NT, KS = Shape<D>::KS, SLOT = Shape<D>::SLOT;
+  using Dma = TileDma<D, 2>;
+  static_assert(NBUF >= 2 && NBUF <= 3, "ring depth");
+  __shared__ __attribute__((aligned(1024))) char ring[NBUF * SLOT];
+
+  const uint32_t xcd = blockIdx.x % 8u, r = blockIdx.x / 8u;
+  const uint32_t start = xcd * pg.per, end = min(pg.total, start + pg.per);
+  if (start + r >= end) return;
+  const int n_items = (int)((end - start - r + pg.g - 1) / pg.g);
+  const int Nb = a.Nb, N = a.N, keep = a.keep;
+  const int total_tiles = n_items * keep;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const float c = a.alpha * kLog2e;
+
+  Dma dma;
+  dma.init(wave, lane);
+  Frag<D> fr;
+  fr.init(ring);
+
+  // DMA cursor: the next tile to request is block dn of query block dk.
+  ItemCtx<D> dit;
+  dit.set(a, start + r);
+  int dk = 0, dn = 0, dslot = 0, issued = 0;
+  auto issue_next = [&]() {
+    dma.issue(ring + dslot * SLOT, dit.kb, dit.vb, dit.block(dn, Nb), N);
+    ++issued;
+    dslot = dslot + 1 == NBUF ? 0 : dslot + 1;
+    if (++dn == keep) {
+      dn = 0;
+      if (++dk < n_items) dit.set(a, start + r + (uint32_t)dk * pg.g);
+    }
+  };
+  for (int t = 0; t < NBUF - 1; ++t)
+    if (t < total_tiles) issue_next();
+
+  ItemCtx<D> it;
+  it.set(a, start + r);
+  Rows<D> st, nx;  // current and next query block's Q operand
+  load_q<D>(nx, it.qb, it.qi * kBlock + wave * 32 + l32, N);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(nx.q[ks]));  // Q of the first block in place
+
+  int slot = 0, consumed = 0;
+  for (int k = 0; k < n_items; ++k) {
+    if (k > 0) it.set(a, start + r + (uint32_t)k * pg.g);
+    const int row = it.qi * kBlock + wave * 32 + l32;
+    const bool row_ok = row < N;
+    const size_t srow = (size_t)it.bh * N + min(row, N - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) st.q[ks] = nx.q[ks];
+    f32x16 o[NT];
+    float z = 0.f;
+    float m_c = 0.f, zf_c = 1.f, zs_c = 1.f;
+    f32x4 rc[NT][4];
+
+    auto step = [&](int n, bool first) {
+      wait_tile<Dma::IPT>(min(NBUF - 2, total_tiles - 1 - consumed));
+      __builtin_amdgcn_s_barrier();
+      if (issued < total_tiles) issue_next();
+      if (first) {
+        // residual and statistics of this block, and Q of the next one; waited for at the next tile
+        m_c = a.m[srow];
+        zf_c = a.z_full[srow];
+        zs_c = a.z_sparse[srow];
+        const float* rrow = a.R + srow * D;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int d = 32 * t + 8 * i4 + 4 * g;
+            rc[t][i4] = d < D ? __builtin_nontemporal_load((const f32x4*)(rrow + d)) : f32x4{};
+          }
+        if (k + 1 < n_items) {
+          ItemCtx<D> nit;
+          nit.set(a, start + r + (uint32_t)(k + 1) * pg.g);
+          load_q<D>(nx, nit.qb, nit.qi * kBlock + wave * 32 + l32, N);
+        }
+      }
+      const uint32_t soff = (uint32_t)slot * SLOT;
+      slot = slot + 1 == NBUF ? 0 : slot + 1;
+      ++consumed;
+      Frag<D> f2;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) f2.k[ks] = fr.k[ks] + soff;
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt) {
+        f2.v[dt][0] = fr.v[dt][0] + soff;
+        f2.v[dt][1] = fr.v[dt][1] + soff;
+      }
+      const int j = it.block(n, Nb);
+      f32x16 s[2];
+      scores<D, 0>(s, st, f2, min(kBlock, N - j * kBlock));
+      if (first) {  // nothing accumulated yet: start from this block's max
+        const float mx = row_max(s);
+        st.m_true = mx;
+        st.m_ref = mx;
+      } else {
+        bool any;
+        const float corr = update_max(st.m_ref, st.m_true, row_max(s), c, &any);
+        if (any) {
+          z *= corr;
+#pragma unroll
+          for (int t = 0; t < NT; ++t) o[t] *= corr;
+        }
+      }
+      u32x2 vh[NT][2][2][2];
+      v_fetch<D, 0>(vh, f2);
+      bf16x8 p[2][2];
+      probs(p, s, st.m_ref, c);
+      z += sum_rounded(p);
+      if (first) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) o[t] = f32x16{};
+      }
+      pv_mfma<D>(o, p, vh);
+    };
+
+    // keep >= 2 here (the launcher sends keep == 1 to the per-block kernel)
+    step(0, true);
+    step(1, false);
+    // The loads issued at the first tile are complete here (the tile wait of
+    // the second tile covered them); using them now keeps the compiler from
+    // waiting for them later, when tile DMA would be in flight.
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) asm volatile("" ::"v"(rc[t][i4]));
+    asm volatile("" ::"v"(m_c), "v"(zf_c), "v"(zs_c));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(nx.q[ks]));
+    for (int n = 2; n < keep; ++n) step(n, false);
+
+    const float zz = pair_sum(z);
+    if (row_ok) {
+      const float m_cur = st.m_ref * a.alpha;
+      const float big = fmaxf(m_cur, m_c);
+      const float e1 = expf(m_cur - big), e2 = expf(m_c - big);
+      const float inv = 1.f / (zz * e1 * zf_c / zs_c);
+      const float w1 = e1 * inv, w2 = e2 * inv;
+      __bf16* orow = (__bf16*)a.o + srow * D;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = 32 * t + 8 * i4 + 4 * g;
+          if (d < D) {
+            __bf16 ob[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ob[e] = (__bf16)(o[t][4 * i4 + e] * w1 + rc[t][i4][e] * w2);
+            *(u32x2*)(orow + d) = *(u32x2*)ob;
+          }
+        }
+    }
   }
 }
 
@@ -629,12 +860,21 @@ __global__ void __launch_bounds__(128 * QB) calib_kernel(AttnArgs a, XcdGrid gri
 
 constexpr int kSparseRing = 2;
 constexpr int kCalibRing = 3;
+constexpr bool kPersistent = true;
+constexpr int kPersistWgPerXcd = 32 * 4;  // 4 two-wave workgroups per CU
 
 template <int D>
 hipError_t launch_d(AttnMode mode, const AttnArgs& a, hipStream_t s) {
   if (mode == AttnMode::kSparse) {
-    XcdGrid grid = make_xcd_grid((uint32_t)a.BH * (uint32_t)a.Nb);
-    hipLaunchKernelGGL((sparse_kernel<D, kSparseRing>), dim3(grid.grid()), dim3(128), 0, s, a, grid);
+    if (kPersistent && a.keep >= 2) {
+      const uint32_t total = (uint32_t)a.BH * (uint32_t)a.Nb;
+      PersistGrid pg{total, (total + 7u) / 8u, 0u};
+      pg.g = min(pg.per, (uint32_t)kPersistWgPerXcd);
+      hipLaunchKernelGGL((sparse_persistent_kernel<D, kSparseRing>), dim3(8u * pg.g), dim3(128), 0, s, a, pg);
+    } else {
+      XcdGrid grid = make_xcd_grid((uint32_t)a.BH * (uint32_t)a.Nb);
+      hipLaunchKernelGGL((sparse_kernel<D, kSparseRing>), dim3(grid.grid()), dim3(128), 0, s, a, grid);
+    }
   } else {
     constexpr int QB = D == 64 ? 4 : 2;  // 2*QB waves must divide the LDS row units
     const uint32_t groups = (uint32_t)(a.Nb + QB - 1) / QB;
