@@ -228,7 +228,7 @@ def main():
                  "frac": round(tflops / PEAK_BF16_TFLOPS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": "rt_sparse_attn_reshape (attn_bf16_kernel<64, sparse>)",
+                     "kernel": "rt_sparse_attn_reshape (sparse_occ_kernel<64>)",
                      "algorithmic_bytes_per_launch": byts},
         "pages_context": {"kept_fraction": round(keep / configs.n_blocks(N), 4),
                           "skipped_fraction": round(1 - flop / (4 * d * N * N * cfg["B"] * cfg["H"]), 4)},

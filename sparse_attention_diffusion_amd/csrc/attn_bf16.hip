@@ -14,19 +14,19 @@
 // so every lane owns one query row (lane % 32) in both results and the row
 // statistics never leave the lane pair (l, l^32).
 //
-// K and V tiles reach LDS by DMA (global_load_lds_dwordx4, no register
-// staging) into a ring of NBUF slots, so NBUF-1 key blocks are in flight while
-// one is consumed; one workgroup barrier per key block.  LDS rows are made of
-// 16-byte units, XOR-swizzled.  All LDS reads of the ring are issued from
-// inline asm that waits for them itself: the compiler would otherwise wait for
-// every DMA in flight before each read (it cannot tell ring slots apart), which
-// would undo the prefetch.  V^T operands come from ds_read_b64_tr_b16.  The
-// softmax reference max is raised lazily (only when a block max exceeds it by
-// more than a factor 2^8 in probability), which keeps the accumulator rescale
-// off the common path.
+// K and V tiles reach LDS by DMA (buffer/global_load ... lds, no register
+// staging).  LDS rows are made of 16-byte units, XOR-swizzled.  All LDS reads
+// of tiles are issued from inline asm that waits for them itself: the
+// compiler would otherwise wait for every DMA in flight before each read (it
+// cannot tell a slot being filled from one being read), which would undo the
+// overlap.  V^T operands come from ds_read_b64_tr_b16.  The softmax reference
+// max is raised lazily (only when a block max exceeds it by more than a factor
+// 2^8 in probability), which keeps the accumulator rescale off the common path.
 //
-// Sparse kernel: one workgroup (2 waves) per 64-row query block; the cached
-// residual and statistics are prefetched into registers at entry.
+// Sparse kernel: persistent, XCD-aware; one K slot and one V slot per
+// two-wave workgroup and at most 128 VGPRs, so that many workgroups share a
+// CU and hide each other's memory latency.  A query block's accumulator
+// starts as its cached residual.
 // Calibration kernel: QB query blocks (2 waves each) share every K/V tile; key
 // blocks are visited in ascending order and each wave adds a block either to
 // its kept accumulator or to its residual accumulator (a wave-uniform choice).
@@ -212,6 +212,35 @@ __device__ __forceinline__ void k_reads(u32x4 (&a)[2 * KS], const uint32_t (&ad)
   }
 }
 
+// K operands of one 32-key half at byte offset `off` from the lane addresses:
+// KS ds_read_b128 waited for in the same statement.
+template <int KS>
+__device__ __forceinline__ void k_half(u32x4 (&a)[KS], const uint32_t (&ad)[KS], uint32_t off) {
+  if constexpr (KS == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+        : "v"(ad[0] + off), "v"(ad[1] + off), "v"(ad[2] + off), "v"(ad[3] + off)
+        : "memory");
+  } else {
+    static_assert(KS == 5, "k-steps");
+    asm volatile(
+        "ds_read_b128 %0, %5\n\t"
+        "ds_read_b128 %1, %6\n\t"
+        "ds_read_b128 %2, %7\n\t"
+        "ds_read_b128 %3, %8\n\t"
+        "ds_read_b128 %4, %9\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4])
+        : "v"(ad[0] + off), "v"(ad[1] + off), "v"(ad[2] + off), "v"(ad[3] + off), "v"(ad[4] + off)
+        : "memory");
+  }
+}
+
 // V^T operands of one d tile for the four k-steps (t, hs): eight
 // ds_read_b64_tr_b16, waited for in the same statement.  h[t][hs][hh].
 template <int OFF, int T, int HS>
@@ -384,329 +413,293 @@ __device__ __forceinline__ void load_q(Rows<D>& st, const char* qbase, int row, 
   st.m_true = -INFINITY;
 }
 
-// ---------------------------------------------------------------- sparse step
-template <int D, int NBUF>
-struct SparseCtx {
-  static constexpr int NT = Shape<D>::NT;
-  using Dma = TileDma<D, 2>;
-  char* ring;
-  const __attribute__((address_space(4))) int32_t* list;  // kept blocks, read with scalar loads
-  const char* kbase;
-  const char* vbase;
-  int keep, N, Nb;
-  float c;
-  Dma dma;
-
-  __device__ __forceinline__ int block_at(int n) const { return min(max(list[n], 0), Nb - 1); }
-  Frag<D> fr;
-  Rows<D> st;
-  f32x16 o[NT];
-  float z;
-
-  // Key block n of the list, in ring slot SLOT = n % NBUF.
-  template <int SLOT>
-  __device__ __forceinline__ void step(int n) {
-    wait_tile<Dma::IPT>(min(NBUF - 2, keep - 1 - n));
-    __builtin_amdgcn_s_barrier();
-    if (n + NBUF - 1 < keep) {
-      constexpr int NEXT = (SLOT + NBUF - 1) % NBUF;
-      dma.issue(ring + NEXT * Shape<D>::SLOT, kbase, vbase, block_at(n + NBUF - 1), N);
-    }
-    const int j = block_at(n);
-    f32x16 s[2];
-    scores<D, SLOT * Shape<D>::SLOT>(s, st, fr, min(kBlock, N - j * kBlock));
-    bool any;
-    const float corr = update_max(st.m_ref, st.m_true, row_max(s), c, &any);
-    if (any) {
-      z *= corr;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) o[t] *= corr;
-    }
-    bf16x8 p[2][2];
-    probs(p, s, st.m_ref, c);
-    z += sum_rounded(p);
-    pv<D, SLOT * Shape<D>::SLOT>(o, p, fr);
-  }
-};
-
-template <int D, int NBUF>
-__global__ void __launch_bounds__(128) sparse_kernel(AttnArgs a, XcdGrid grid) {
-  constexpr int NT = Shape<D>::NT;
-  static_assert(NBUF >= 2 && NBUF <= 3, "ring depth");
-  __shared__ __attribute__((aligned(1024))) char ring[NBUF * Shape<D>::SLOT];
-
-  const uint32_t lin = grid.linear(blockIdx.x);
-  if (lin >= grid.total) return;
-  const int Nb = a.Nb, N = a.N, keep = a.keep;
-  const int bh = lin / Nb, qi = lin % Nb;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 5, l32 = lane & 31;
-  const size_t head = (size_t)bh * N * D;
-  const int row = qi * kBlock + wave * 32 + l32;
-  const bool row_ok = row < N;
-  const size_t srow = (size_t)bh * N + (row_ok ? row : N - 1);
-
-  // Memory order: the first tiles (their block indices come from scalar loads
-  // of the list), then Q, then the statistics and the residual (needed last).
-  SparseCtx<D, NBUF> cx;
-  cx.ring = ring;
-  cx.list = (const __attribute__((address_space(4))) int32_t*)(a.idx + ((size_t)bh * Nb + qi) * keep);
-  cx.kbase = (const char*)a.k + head * 2;
-  cx.vbase = (const char*)a.v + head * 2;
-  cx.keep = keep;
-  cx.N = N;
-  cx.Nb = Nb;
-  cx.c = a.alpha * kLog2e;
-  cx.dma.init(wave, lane);
-  cx.fr.init(ring);
-#pragma unroll
-  for (int t = 0; t < NBUF - 1; ++t)
-    if (t < keep) cx.dma.issue(ring + t * Shape<D>::SLOT, cx.kbase, cx.vbase, cx.block_at(t), N);
-  load_q<D>(cx.st, (const char*)a.q + head * 2, row, N);
-
-  const float m_c = a.m[srow], zf_c = a.z_full[srow], zs_c = a.z_sparse[srow];
-  f32x4 rc[NT][4];
-  {
-    const float* rrow = a.R + srow * D;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = 32 * t + 8 * i4 + 4 * g;
-        rc[t][i4] = d < D ? __builtin_nontemporal_load((const f32x4*)(rrow + d)) : f32x4{};
-      }
-  }
-
-#pragma unroll
-  for (int t = 0; t < NT; ++t) cx.o[t] = f32x16{};
-  cx.z = 0.f;
-  for (int n = 0; n < keep; n += NBUF) {
-    cx.template step<0>(n);
-    if (n + 1 < keep) cx.template step<1>(n + 1);
-    if constexpr (NBUF > 2)
-      if (n + 2 < keep) cx.template step<2>(n + 2);
-  }
-
-  // O = (N e^{m-M} + R_c e^{m_c-M}) / (Z e^{m-M} Z_full_c / Z_sparse_c), M = max(m, m_c);
-  // N and Z are relative to m = the reference max (any reference gives the same O).
-  const float z = pair_sum(cx.z);
-  if (row_ok) {
-    const float m_cur = cx.st.m_ref * a.alpha;
-    const float big = fmaxf(m_cur, m_c);
-    const float e1 = expf(m_cur - big), e2 = expf(m_c - big);
-    const float inv = 1.f / (z * e1 * zf_c / zs_c);
-    const float w1 = e1 * inv, w2 = e2 * inv;
-    __bf16* orow = (__bf16*)a.o + srow * D;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = 32 * t + 8 * i4 + 4 * g;
-        if (d < D) {
-          __bf16 ob[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ob[e] = (__bf16)(cx.o[t][4 * i4 + e] * w1 + rc[t][i4][e] * w2);
-          *(u32x2*)(orow + d) = *(u32x2*)ob;
-        }
-      }
-  }
-}
-
-// ---------------------------------------------------------------- sparse step, persistent
-// A persistent variant of the sparse step: each workgroup walks a strided run
-// of query blocks (all from its XCD's range) and feeds one continuous stream of
-// key-block tiles through the ring, so the next query block's first tiles are
-// already in flight while the current one finishes, and the per-block setup
-// (list, Q, residual) overlaps with compute:
-//   * Q of the next query block is loaded into a second register set one
-//     block ahead;
-//   * the residual and statistics of the current block are loaded right after
-//     its first tile is consumed and waited for at its second tile;
-//   * the block index of every tile comes from scalar loads of the list.
-// Tiles are numbered T = k*keep + n over the workgroup's k-th query block.
+// Persistent grid: each of the 8 XCDs owns a contiguous range of `per` query
+// blocks (blocks of a range share heads, hence K/V tiles in that XCD's L2);
+// its `g` workgroups walk the range with stride g.
 struct PersistGrid {
   uint32_t total, per, g;  // query blocks, per XCD, workgroups per XCD
 };
 
-// Scalar context of one query block of the persistent walk.
+// ---------------------------------------------------------------- buffer-resource helpers
+// Global traffic of the sparse kernel goes through buffer resources: per-lane
+// offsets are fixed, the base and the byte limit are scalar, and the limit
+// zero-fills rows past N on loads and drops them on stores.
+constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format (descriptor word 3)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufFlags);
+}
+
+
+// Tile DMA of one K or V tile, this wave's half (RSU/2 instructions of 1 KB);
+// same unit placement as TileDma.
 template <int D>
-struct ItemCtx {
-  const __attribute__((address_space(4))) int32_t* list;  // its kept blocks (scalar loads)
-  const char* kb;                                          // K, V, Q of its head
-  const char* vb;
-  const char* qb;
-  uint32_t lin;
-  int qi, bh;
+struct PipeDma {
+  static constexpr int RSU = Shape<D>::RSU;
+  static constexpr int NI = RSU / 2;
+  uint32_t off[NI];
+  int wave;
+  __device__ __forceinline__ void init(int w, int lane) {
+    wave = w;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int L = 64 * (w + 2 * i) + lane;
+      const int r = L / RSU, p = L % RSU;
+      int u = p < 8 ? (p ^ swz(r)) : p;
+      if (u >= Shape<D>::UNITS) u -= 2;  // filler units of d_pad = 80 rows: any finite data
+      off[i] = (uint32_t)((r * D + u * 8) * 2);
+    }
+  }
+  // Rows of key block j of one head (K or V at `head`) into `slot`; rows past
+  // N are zero-filled by the buffer limit.
+  __device__ __forceinline__ void issue(char* slot, const char* head, int j, int N) const {
+    const int rows = min(N - j * kBlock, kBlock);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(head + (size_t)j * kBlock * D * 2, rows * D * 2);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + (wave + 2 * i) * 1024), 16, off[i], 0, 0, 0);
+  }
+};
+
+// Scalar context of one query block: its kept list and its head.
+template <int D>
+struct PipeItem {
+  const __attribute__((address_space(4))) int32_t* list;
+  const char* kh;
+  const char* vh;
+  int bh, qi;
   __device__ __forceinline__ void set(const AttnArgs& a, uint32_t l) {
-    lin = l;
     bh = (int)(l / (uint32_t)a.Nb);
     qi = (int)(l - (uint32_t)bh * (uint32_t)a.Nb);
     const size_t head = (size_t)bh * a.N * D * 2;
-    kb = (const char*)a.k + head;
-    vb = (const char*)a.v + head;
-    qb = (const char*)a.q + head;
+    kh = (const char*)a.k + head;
+    vh = (const char*)a.v + head;
     list = (const __attribute__((address_space(4))) int32_t*)(a.idx + (size_t)l * a.keep);
   }
   __device__ __forceinline__ int block(int n, int Nb) const { return min(max(list[n], 0), Nb - 1); }
 };
 
-template <int D, int NBUF>
-__global__ void __launch_bounds__(128) sparse_persistent_kernel(AttnArgs a, PersistGrid pg) {
-  constexpr int NT = Shape<D>::NT, KS = Shape<D>::KS, SLOT = Shape<D>::SLOT;
-  using Dma = TileDma<D, 2>;
-  static_assert(NBUF >= 2 && NBUF <= 3, "ring depth");
-  __shared__ __attribute__((aligned(1024))) char ring[NBUF * SLOT];
+// One query block's per-lane data, loaded a block ahead: Q^T operand,
+// statistics and residual (in accumulator order).  KS + 3 + D/8 loads.
+template <int D>
+struct PipeStats {
+  float mc, zf, zs;
+};
 
-  const uint32_t xcd = blockIdx.x % 8u, r = blockIdx.x / 8u;
+template <int D>
+__device__ __forceinline__ void pipe_load(bf16x8 (&q)[Shape<D>::KS], PipeStats<D>& st, f32x4 (&r)[Shape<D>::NT][4],
+                                          const AttnArgs& a, int bh, int qi, int rowq, int g) {
+  const size_t r0 = (size_t)bh * a.N + (size_t)qi * kBlock;  // first row of the block
+  const int rows = min(a.N - qi * kBlock, kBlock);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)a.q + r0 * D * 2, rows * D * 2);
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.R + r0 * D, rows * D * 4);
+#pragma unroll
+  for (int ks = 0; ks < Shape<D>::KS; ++ks)
+    q[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, (rowq * D + 16 * ks + 8 * g) * 2, 0, 0));
+  st.mc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.m + r0, rows * 4), rowq * 4, 0, 0));
+  st.zf = __builtin_bit_cast(float,
+                             __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.z_full + r0, rows * 4), rowq * 4, 0, 0));
+  st.zs = __builtin_bit_cast(float,
+                             __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.z_sparse + r0, rows * 4), rowq * 4, 0, 0));
+#pragma unroll
+  for (int t = 0; t < Shape<D>::NT; ++t)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      if (32 * t + 8 * i4 < D)
+        r[t][i4] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, (rowq * D + 32 * t + 8 * i4 + 4 * g) * 4, 0, 0));
+      else
+        r[t][i4] = f32x4{};
+    }
+}
+
+// O^T += V^T P^T with the V operands already fetched.
+template <int D>
+__device__ __forceinline__ void mask_keys(f32x16 (&s)[2], int nvalid) {
+  const int g = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = 32 * t + (i >> 2) * 8 + 4 * g + (i & 3);
+      if (key >= nvalid) s[t][i] = -INFINITY;
+    }
+}
+
+// P = exp2(c s - mr) as bf16 MFMA operands (mr: reference max times c).
+__device__ __forceinline__ void probs_ref(bf16x8 (&p)[2][2], const f32x16 (&s)[2], float mr, float c) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[t][i >> 3][i & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[t][i], c, -mr));
+}
+
+// ---------------------------------------------------------------- sparse step, high occupancy
+// The production sparse kernel.  One K slot and one V slot per workgroup
+// (16 KB for d_pad 64) and at most 128 VGPRs per lane, so that 8 two-wave
+// workgroups share a CU (4 waves per SIMD): the latency of tile DMA and of the
+// per-query-block loads is hidden by the other workgroups instead of by a
+// deep ring, which the LDS could not hold (each wave's vmcnt is one in-order
+// counter, so any long-latency load a wave issues delays its next tile wait).
+// Per key block n of a query block:
+//   1. wait for K_n, barrier (V_{n-1} consumed by both waves), DMA V_n;
+//   2. S^T = K_n Q^T in two 32-key halves, softmax with the lazy max;
+//   3. wait for V_n, barrier (K_n consumed), DMA K_{n+1} (which may belong to
+//      the next query block);
+//   4. O^T += V_n^T P^T.
+// A query block's accumulator starts as its cached residual R with the
+// reference max at the cached m (R is stored relative to m); the lazy max
+// update rescales both parts together, so the reshape epilogue is
+// O = acc * Z_sparse / (Z * Z_full) with Z the kept mass.  All global traffic
+// goes through buffer resources whose byte limit zero-fills rows past N on
+// loads and drops them on stores.
+template <int D>
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 3, 4)))
+sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
+  constexpr int NT = Shape<D>::NT, KS = Shape<D>::KS, TILE = Shape<D>::TILE, ROW = Shape<D>::ROW;
+  constexpr int NST = D / 8;          // O stores (and residual loads) per lane
+  constexpr int NLD = KS + NST + 3;   // per-query-block loads (Q, residual, statistics)
+  __shared__ __attribute__((aligned(1024))) char ring[2 * TILE];  // K slot, V slot
+  char* const kslot = ring;
+  char* const vslot = ring + TILE;
+
+  const uint32_t xcd = blockIdx.x % 8u, rr = blockIdx.x / 8u;
   const uint32_t start = xcd * pg.per, end = min(pg.total, start + pg.per);
-  if (start + r >= end) return;
-  const int n_items = (int)((end - start - r + pg.g - 1) / pg.g);
+  if (start + rr >= end) return;
+  const int n_items = (int)((end - start - rr + pg.g - 1) / pg.g);
   const int Nb = a.Nb, N = a.N, keep = a.keep;
-  const int total_tiles = n_items * keep;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 5, l32 = lane & 31, G = lane >> 4, i16 = lane & 15;
+  const int rowq = wave * 32 + l32;  // row within the query block
   const float c = a.alpha * kLog2e;
+  auto item_at = [&](int k) { return start + rr + (uint32_t)k * pg.g; };
 
-  Dma dma;
+  // LDS that no DMA has written yet must still read as finite numbers.
+  {
+    const u32x4 zero = {};
+#pragma unroll
+    for (int i = 0; i < 2 * TILE / (16 * 128); ++i) *(u32x4*)(ring + (i * 128 + (int)threadIdx.x) * 16) = zero;
+    __syncthreads();
+  }
+
+  PipeDma<D> dma;
   dma.init(wave, lane);
-  Frag<D> fr;
-  fr.init(ring);
-
-  // DMA cursor: the next tile to request is block dn of query block dk.
-  ItemCtx<D> dit;
-  dit.set(a, start + r);
-  int dk = 0, dn = 0, dslot = 0, issued = 0;
-  auto issue_next = [&]() {
-    dma.issue(ring + dslot * SLOT, dit.kb, dit.vb, dit.block(dn, Nb), N);
-    ++issued;
-    dslot = dslot + 1 == NBUF ? 0 : dslot + 1;
-    if (++dn == keep) {
-      dn = 0;
-      if (++dk < n_items) dit.set(a, start + r + (uint32_t)dk * pg.g);
+  uint32_t ka[KS], va[NT][2];  // LDS addresses of this lane's K and V^T operands
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) ka[ks] = lds_addr(kslot) + lds_off<D>(l32, 2 * ks + g);
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      // ds_read_b64_tr_b16 transposes within 16-lane groups: lane i of a group
+      // points at key kbase + i/4, columns 4(i%4)..+3, and receives column i of
+      // keys kbase..kbase+3.
+      const int key = 8 * hh + 4 * g + (i16 >> 2);
+      const int doff = 32 * dt + 16 * (G & 1) + 4 * (i16 & 3);
+      va[dt][hh] = lds_addr(vslot) + lds_off<D>(key, doff >> 3) + (doff & 7) * 2;
     }
-  };
-  for (int t = 0; t < NBUF - 1; ++t)
-    if (t < total_tiles) issue_next();
 
-  ItemCtx<D> it;
-  it.set(a, start + r);
-  Rows<D> st, nx;  // current and next query block's Q operand
-  load_q<D>(nx, it.qb, it.qi * kBlock + wave * 32 + l32, N);
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(nx.q[ks]));  // Q of the first block in place
+  PipeItem<D> it;
+  it.set(a, item_at(0));
+  int j = it.block(0, Nb);
+  dma.issue(kslot, it.kh, j, N);  // K of the first tile
 
-  int slot = 0, consumed = 0;
-  for (int k = 0; k < n_items; ++k) {
-    if (k > 0) it.set(a, start + r + (uint32_t)k * pg.g);
-    const int row = it.qi * kBlock + wave * 32 + l32;
-    const bool row_ok = row < N;
-    const size_t srow = (size_t)it.bh * N + min(row, N - 1);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) st.q[ks] = nx.q[ks];
-    f32x16 o[NT];
-    float z = 0.f;
-    float m_c = 0.f, zf_c = 1.f, zs_c = 1.f;
-    f32x4 rc[NT][4];
-
-    auto step = [&](int n, bool first) {
-      wait_tile<Dma::IPT>(min(NBUF - 2, total_tiles - 1 - consumed));
-      __builtin_amdgcn_s_barrier();
-      if (issued < total_tiles) issue_next();
-      if (first) {
-        // residual and statistics of this block, and Q of the next one; waited for at the next tile
-        m_c = a.m[srow];
-        zf_c = a.z_full[srow];
-        zs_c = a.z_sparse[srow];
-        const float* rrow = a.R + srow * D;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4) {
-            const int d = 32 * t + 8 * i4 + 4 * g;
-            rc[t][i4] = d < D ? __builtin_nontemporal_load((const f32x4*)(rrow + d)) : f32x4{};
-          }
-        if (k + 1 < n_items) {
-          ItemCtx<D> nit;
-          nit.set(a, start + r + (uint32_t)(k + 1) * pg.g);
-          load_q<D>(nx, nit.qb, nit.qi * kBlock + wave * 32 + l32, N);
-        }
-      }
-      const uint32_t soff = (uint32_t)slot * SLOT;
-      slot = slot + 1 == NBUF ? 0 : slot + 1;
-      ++consumed;
-      Frag<D> f2;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) f2.k[ks] = fr.k[ks] + soff;
-#pragma unroll
-      for (int dt = 0; dt < NT; ++dt) {
-        f2.v[dt][0] = fr.v[dt][0] + soff;
-        f2.v[dt][1] = fr.v[dt][1] + soff;
-      }
-      const int j = it.block(n, Nb);
-      f32x16 s[2];
-      scores<D, 0>(s, st, f2, min(kBlock, N - j * kBlock));
-      if (first) {  // nothing accumulated yet: start from this block's max
-        const float mx = row_max(s);
-        st.m_true = mx;
-        st.m_ref = mx;
-      } else {
-        bool any;
-        const float corr = update_max(st.m_ref, st.m_true, row_max(s), c, &any);
-        if (any) {
-          z *= corr;
-#pragma unroll
-          for (int t = 0; t < NT; ++t) o[t] *= corr;
-        }
-      }
-      u32x2 vh[NT][2][2][2];
-      v_fetch<D, 0>(vh, f2);
-      bf16x8 p[2][2];
-      probs(p, s, st.m_ref, c);
-      z += sum_rounded(p);
-      if (first) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) o[t] = f32x16{};
-      }
-      pv_mfma<D>(o, p, vh);
-    };
-
-    // keep >= 2 here (the launcher sends keep == 1 to the per-block kernel)
-    step(0, true);
-    step(1, false);
-    // The loads issued at the first tile are complete here (the tile wait of
-    // the second tile covered them); using them now keeps the compiler from
-    // waiting for them later, when tile DMA would be in flight.
+  bf16x8 q[KS];
+  f32x16 o[NT];
+  PipeStats<D> st;
+  // Q, statistics and residual (straight into the accumulator) of query block
+  // `it`: NLD loads.
+  auto load_rows = [&]() {
+    f32x4 r[NT][4];
+    pipe_load<D>(q, st, r, a, it.bh, it.qi, rowq, g);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) asm volatile("" ::"v"(rc[t][i4]));
-    asm volatile("" ::"v"(m_c), "v"(zf_c), "v"(zs_c));
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(nx.q[ks]));
-    for (int n = 2; n < keep; ++n) step(n, false);
+      for (int i = 0; i < 16; ++i) o[t][i] = r[t][i >> 2][i & 3];
+  };
+  load_rows();
 
-    const float zz = pair_sum(z);
-    if (row_ok) {
-      const float m_cur = st.m_ref * a.alpha;
-      const float big = fmaxf(m_cur, m_c);
-      const float e1 = expf(m_cur - big), e2 = expf(m_c - big);
-      const float inv = 1.f / (zz * e1 * zf_c / zs_c);
-      const float w1 = e1 * inv, w2 = e2 * inv;
-      __bf16* orow = (__bf16*)a.o + srow * D;
+  for (int k = 0; k < n_items; ++k) {
+    float mr = st.mc * kLog2e, z = 0.f;
+    for (int n = 0; n < keep; ++n) {
+      // 1. K_n has landed (the loads issued after it may still be in flight).
+      if (n == 0 && k > 0) wait_vmcnt<NST + NLD>();
+      else if (n == 0) wait_vmcnt<NLD>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      dma.issue(vslot, it.vh, j, N);
+      const int nvalid = N - j * kBlock;
+      // 2. scores and P, one 32-key half at a time.
+      f32x16 s[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        u32x4 kk[KS];
+        k_half<KS>(kk, ka, t * 32 * ROW);
+        s[t] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kk[ks]), q[ks], s[t], 0, 0, 0);
+      }
+      if (nvalid < kBlock) mask_keys<D>(s, nvalid);
+      const float mx = row_max(s) * c;
+      if (__ballot(mx > mr + kLazyLog2) != 0ull) {
+        const float mnew = fmaxf(mr, mx);
+        const float corr = __builtin_amdgcn_exp2f(mr - mnew);
+        mr = mnew;
+        z *= corr;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) o[t] *= corr;
+      }
+      bf16x8 p[2][2];
+      probs_ref(p, s, mr, c);
+      z += sum_rounded(p);
+      // 3. V_n has landed; K_n is consumed: K of the next tile goes out.
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      const bool last = n == keep - 1;
+      if (!last) {
+        j = it.block(n + 1, Nb);
+        dma.issue(kslot, it.kh, j, N);
+      } else if (k + 1 < n_items) {
+        PipeItem<D> nit;
+        nit.set(a, item_at(k + 1));
+        j = nit.block(0, Nb);
+        dma.issue(kslot, nit.kh, j, N);
+      }
+      // 4. P.V, one d tile at a time.
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt) {
+        u32x2 h[2][2][2];
+        tr_reads<0, 32 * ROW, 16 * ROW>(h, va[dt][0], va[dt][1]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs) {
+            const u32x4 both = __builtin_shufflevector(h[t][hs][0], h[t][hs][1], 0, 1, 2, 3);
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), p[t][hs], o[dt], 0, 0, 0);
+          }
+      }
+    }
+    // O = acc * Z_sparse / (Z * Z_full); rows past N are dropped by the limit.
+    {
+      const float w = st.zs / (pair_sum(z) * st.zf);
+      const size_t r0 = (size_t)it.bh * N + (size_t)it.qi * kBlock;
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc((const char*)a.o + r0 * D * 2, min(N - it.qi * kBlock, kBlock) * D * 2);
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d = 32 * t + 8 * i4 + 4 * g;
-          if (d < D) {
+        for (int i4 = 0; i4 < 4; ++i4)
+          if (32 * t + 8 * i4 < D) {
             __bf16 ob[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ob[e] = (__bf16)(o[t][4 * i4 + e] * w1 + rc[t][i4][e] * w2);
-            *(u32x2*)(orow + d) = *(u32x2*)ob;
+            for (int e = 0; e < 4; ++e) ob[e] = (__bf16)(o[t][4 * i4 + e] * w);
+            __builtin_amdgcn_raw_buffer_store_b64(*(u32x2*)ob, ro, (rowq * D + 32 * t + 8 * i4 + 4 * g) * 2, 0, 0);
           }
-        }
+    }
+    if (k + 1 < n_items) {
+      it.set(a, item_at(k + 1));
+      load_rows();
     }
   }
 }
@@ -858,23 +851,19 @@ __global__ void __launch_bounds__(128 * QB) calib_kernel(AttnArgs a, XcdGrid gri
   }
 }
 
-constexpr int kSparseRing = 2;
 constexpr int kCalibRing = 3;
-constexpr bool kPersistent = true;
-constexpr int kPersistWgPerXcd = 32 * 4;  // 4 two-wave workgroups per CU
+// Sparse kernel workgroups per XCD: 7 per CU for d_pad 64 (16 KB of LDS and
+// <= 128 VGPRs each would allow 8; 7 measured faster), 6 for d_pad 80.
+constexpr int kSparseWgPerXcd64 = 32 * 7;
+constexpr int kSparseWgPerXcd80 = 32 * 6;
 
 template <int D>
 hipError_t launch_d(AttnMode mode, const AttnArgs& a, hipStream_t s) {
   if (mode == AttnMode::kSparse) {
-    if (kPersistent && a.keep >= 2) {
-      const uint32_t total = (uint32_t)a.BH * (uint32_t)a.Nb;
-      PersistGrid pg{total, (total + 7u) / 8u, 0u};
-      pg.g = min(pg.per, (uint32_t)kPersistWgPerXcd);
-      hipLaunchKernelGGL((sparse_persistent_kernel<D, kSparseRing>), dim3(8u * pg.g), dim3(128), 0, s, a, pg);
-    } else {
-      XcdGrid grid = make_xcd_grid((uint32_t)a.BH * (uint32_t)a.Nb);
-      hipLaunchKernelGGL((sparse_kernel<D, kSparseRing>), dim3(grid.grid()), dim3(128), 0, s, a, grid);
-    }
+    const uint32_t total = (uint32_t)a.BH * (uint32_t)a.Nb;
+    PersistGrid pg{total, (total + 7u) / 8u, 0u};
+    pg.g = min(pg.per, (uint32_t)(D == 64 ? kSparseWgPerXcd64 : kSparseWgPerXcd80));
+    hipLaunchKernelGGL((sparse_occ_kernel<D>), dim3(8u * pg.g), dim3(128), 0, s, a, pg);
   } else {
     constexpr int QB = D == 64 ? 4 : 2;  // 2*QB waves must divide the LDS row units
     const uint32_t groups = (uint32_t)(a.Nb + QB - 1) / QB;
