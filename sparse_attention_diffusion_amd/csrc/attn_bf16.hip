@@ -851,10 +851,10 @@ __global__ void __launch_bounds__(128 * QB) calib_kernel(AttnArgs a, XcdGrid gri
   }
 }
 
-constexpr int kCalibRing = 3;
-// Sparse kernel workgroups per XCD: 7 per CU for d_pad 64 (16 KB of LDS and
-// <= 128 VGPRs each would allow 8; 7 measured faster), 6 for d_pad 80.
-constexpr int kSparseWgPerXcd64 = 32 * 7;
+constexpr int kCalibRing = 2;
+// Sparse kernel workgroups per XCD: 8 per CU for d_pad 64 (16 KB of LDS and
+// <= 128 VGPRs each), 6 for d_pad 80 (24 KB, <= 168 VGPRs).
+constexpr int kSparseWgPerXcd64 = 32 * 8;
 constexpr int kSparseWgPerXcd80 = 32 * 6;
 
 template <int D>
@@ -865,7 +865,7 @@ hipError_t launch_d(AttnMode mode, const AttnArgs& a, hipStream_t s) {
     pg.g = min(pg.per, (uint32_t)(D == 64 ? kSparseWgPerXcd64 : kSparseWgPerXcd80));
     hipLaunchKernelGGL((sparse_occ_kernel<D>), dim3(8u * pg.g), dim3(128), 0, s, a, pg);
   } else {
-    constexpr int QB = D == 64 ? 4 : 2;  // 2*QB waves must divide the LDS row units
+    constexpr int QB = 2;  // 2*QB waves must divide the LDS row units; 2 workgroups per CU
     const uint32_t groups = (uint32_t)(a.Nb + QB - 1) / QB;
     XcdGrid grid = make_xcd_grid((uint32_t)a.BH * groups);
     hipLaunchKernelGGL((calib_kernel<D, kCalibRing, QB>), dim3(grid.grid()), dim3(128 * QB), 0, s, a, grid);
