@@ -450,11 +450,10 @@ struct PipeDma {
       off[i] = (uint32_t)((r * D + u * 8) * 2);
     }
   }
-  // Rows of key block j of one head (K or V at `head`) into `slot`; rows past
-  // N are zero-filled by the buffer limit.
-  __device__ __forceinline__ void issue(char* slot, const char* head, int j, int N) const {
-    const int rows = min(N - j * kBlock, kBlock);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(head + (size_t)j * kBlock * D * 2, rows * D * 2);
+  // A key-block tile (K or V) at `tile`, `bytes` of it valid, into `slot`;
+  // rows past the valid bytes are zero-filled by the buffer limit.
+  __device__ __forceinline__ void issue_at(char* slot, const char* tile, int bytes) const {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, bytes);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + (wave + 2 * i) * 1024), 16, off[i], 0, 0, 0);
@@ -600,10 +599,17 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
       va[dt][hh] = lds_addr(vslot) + lds_off<D>(key, doff >> 3) + (doff & 7) * 2;
     }
 
-  PipeItem<D> it;
+  PipeItem<D> it, nit;  // query block being computed, and the next one
   it.set(a, item_at(0));
+  nit.set(a, item_at(min(1, n_items - 1)));
+  // Tile whose K went out last: its V tile and valid bytes.  The block index
+  // of the tile after it is read one tile ahead (scalar loads: no wait at use).
+  const size_t blk = (size_t)kBlock * D * 2;
   int j = it.block(0, Nb);
-  dma.issue(kslot, it.kh, j, N);  // K of the first tile
+  int jnext = keep > 1 ? it.block(1, Nb) : nit.block(0, Nb);
+  int tbytes = min(N - j * kBlock, kBlock) * D * 2;
+  const char* vtile = it.vh + (size_t)j * blk;
+  dma.issue_at(kslot, it.kh + (size_t)j * blk, tbytes);  // K of the first tile
 
   bf16x8 q[KS];
   f32x16 o[NT];
@@ -628,8 +634,8 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
       else if (n == 0) wait_vmcnt<NLD>();
       else wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
-      dma.issue(vslot, it.vh, j, N);
-      const int nvalid = N - j * kBlock;
+      dma.issue_at(vslot, vtile, tbytes);
+      const int nvalid = tbytes / (D * 2);
       // 2. scores and P, one 32-key half at a time.
       f32x16 s[2];
 #pragma unroll
@@ -657,15 +663,21 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
       // 3. V_n has landed; K_n is consumed: K of the next tile goes out.
       wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
-      const bool last = n == keep - 1;
-      if (!last) {
-        j = it.block(n + 1, Nb);
-        dma.issue(kslot, it.kh, j, N);
-      } else if (k + 1 < n_items) {
-        PipeItem<D> nit;
-        nit.set(a, item_at(k + 1));
-        j = nit.block(0, Nb);
-        dma.issue(kslot, nit.kh, j, N);
+      if (n + 1 < keep || k + 1 < n_items) {
+        const bool same = n + 1 < keep;  // the next tile is in this query block
+        j = jnext;
+        tbytes = min(N - j * kBlock, kBlock) * D * 2;
+        vtile = (same ? it.vh : nit.vh) + (size_t)j * blk;
+        dma.issue_at(kslot, (same ? it.kh : nit.kh) + (size_t)j * blk, tbytes);
+        // block index of the tile after it
+        if (n + 2 < keep) jnext = it.block(n + 2, Nb);
+        else if (n + 2 == keep) jnext = nit.block(0, Nb);
+        else if (keep > 1) jnext = nit.block(1, Nb);
+        else {  // one block per query block: the block after next
+          PipeItem<D> t2;
+          t2.set(a, item_at(min(k + 2, n_items - 1)));
+          jnext = t2.block(0, Nb);
+        }
       }
       // 4. P.V, one d tile at a time.
 #pragma unroll
@@ -698,7 +710,8 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
           }
     }
     if (k + 1 < n_items) {
-      it.set(a, item_at(k + 1));
+      it = nit;
+      nit.set(a, item_at(min(k + 2, n_items - 1)));
       load_rows();
     }
   }

@@ -305,6 +305,59 @@ def test_edge_shapes(N, d, D, keep, forced, dtype):
     assert np.array_equal(idx.cpu().numpy(), ref_idx)
 
 
+@pytest.mark.parametrize("keep", [1, 2, 3, 9])
+def test_sparse_many_blocks_per_workgroup(keep):
+    """The sparse kernel where each persistent workgroup walks several query
+    blocks (so the prefetch of the next block's tiles, lists and rows crosses
+    block boundaries), against the oracle's reshape on sampled query blocks.
+    The statistics cache is synthetic: any positive Z_full >= Z_sparse, any m
+    and any R give a well-defined reshape, and m spans values far below and
+    above the new scores (exercising the lazy max from the cached reference)."""
+    say("sparse many blocks per workgroup", keep)
+    B, H, d = 2, 16, 64
+    N = 64 * 170 + 23  # ragged last block
+    nb = (N + 63) // 64
+    q, k, v = synth.random_qkv(B, H, N, d, d, seed=70 + keep, scale=1.5, dtype="bf16", device=gu.DEV)
+    g = np.random.default_rng(keep)
+    idx = np.stack([np.sort(g.choice(nb, keep, replace=False)) for _ in range(B * H * nb)])
+    idx = idx.reshape(B, H, nb, keep).astype(np.int32)
+    idx[0, 0, :, -1] = nb - 1  # the ragged block in every list of one head
+    idx[0, 0] = np.sort(idx[0, 0], axis=-1)
+    for a in range(nb):  # keep lists of distinct blocks
+        row = np.unique(idx[0, 0, a])
+        while len(row) < keep:
+            row = np.unique(np.append(row, g.integers(nb)))
+        idx[0, 0, a] = row
+    m_c = g.uniform(-2.0, 6.0, (B, H, N))
+    z_s = g.uniform(0.5, 2.0, (B, H, N))
+    z_f = z_s * g.uniform(1.0, 4.0, (B, H, N))
+    r_c = g.normal(0.0, 0.5, (B, H, N, d))
+    sh = rettn.shape(B, H, N, d, d, keep, "bf16")
+    cache = rettn.StatsCache(sh, 1)
+    t = cache.tensors(0)
+    t["m"].copy_(torch.as_tensor(m_c, dtype=torch.float32))
+    t["z_full"].copy_(torch.as_tensor(z_f, dtype=torch.float32))
+    t["z_sparse"].copy_(torch.as_tensor(z_s, dtype=torch.float32))
+    t["R"].copy_(torch.as_tensor(r_c, dtype=torch.float32))
+    t["idx"].copy_(torch.as_tensor(idx))
+    cache.set_valid(0)
+    o = gu.sparse(sh, q, k, v, cache)
+    torch.cuda.synchronize()
+    # the oracle reads the statistics as stored (float32)
+    m32, zf32, zs32, r32 = (x.astype(np.float32) for x in (m_c, z_f, z_s, r_c))
+    qh, kh, vh, oh = gu.host(q), gu.host(k), gu.host(v), gu.host(o)
+    got, ref = [], []
+    for b in range(B):
+        for h in range(H):
+            for a in list(g.choice(nb - 1, 3, replace=False)) + [nb - 1]:
+                rows = slice(64 * a, min(64 * a + 64, N))
+                ref.append(oracle.sparse_reshape_rows(qh[b, h], kh[b, h], vh[b, h], rows, idx[b, h, a],
+                                                      m32[b, h, rows], zf32[b, h, rows], zs32[b, h, rows],
+                                                      r32[b, h, rows], N, d))
+                got.append(oh[b, h, rows])
+    gu.assert_close(np.concatenate(got), np.concatenate(ref))
+
+
 def test_deterministic_bitwise():
     say("determinism")
     cfg = small_cfg("pixart1024", H=4)
