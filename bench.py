@@ -41,6 +41,11 @@ def parse():
     p.add_argument("--cpu-budget-s", type=float, default=10.0)
     p.add_argument("--traffic-probe", action="store_true",
                    help="first run a plain 512 MiB device copy (reference for HBM byte counters)")
+    p.add_argument("--no-components", action="store_true",
+                   help="skip the per-kernel breakdown (selector, calibration, warm/cold sparse)")
+    p.add_argument("--all-configs", action="store_true",
+                   help="print the per-kernel breakdown of every configuration, one JSON line each "
+                        "(not the headline line)")
     return p.parse_args()
 
 
@@ -118,6 +123,78 @@ def cpu_baseline(cfg, heads, budget_s):
     }
 
 
+def components(cfg, reps=20, flush_mb=512):
+    """Per-kernel breakdown on one configuration, from step-0 and step-1 inputs:
+    the selector (rt_select_blocks) with its HBM bytes, the calibration kernel
+    with its dense FLOPs, and the sparse kernel warm (the same inputs call after
+    call) and cold (a write of `flush_mb` MB between calls, larger than the
+    256 MB last-level cache).  Each call is bracketed by HIP events on its
+    stream; medians are reported."""
+    import numpy as np
+    import torch
+    from sparse_attention_diffusion_amd import configs, rettn, synth
+    dev = torch.device("cuda:0")
+    sh = rettn.shape_of(cfg)
+    N, d, D, keep = cfg["N"], cfg["d"], cfg["d_pad"], cfg["keep"]
+    forced = configs.forced_blocks(cfg)
+    it = synth.StepInputs(cfg, seed=0, device=dev)
+    (q0, k0, v0), (q1, k1, v1) = [tuple(synth.store(x, cfg["dtype"]) for x in it.next()) for _ in range(2)]
+    del it
+    ebytes = 2 if cfg["dtype"] == "bf16" else 4
+    nb = configs.n_blocks(N)
+    idx = torch.empty((sh.B, sh.H, nb, keep), dtype=torch.int32, device=dev)
+    ws = torch.empty(rettn.select_workspace_bytes(sh), dtype=torch.uint8, device=dev)
+    out = torch.empty((sh.B, sh.H, N, D), dtype=rettn.torch_dtype(sh), device=dev)
+    cache = rettn.StatsCache(sh, 1, device=dev)
+    flush = torch.empty(flush_mb << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n, cold=False):
+        ms = []
+        for _ in range(n):
+            if cold:
+                flush.fill_(0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms)), [round(float(np.percentile(ms, p)), 5) for p in (10, 50, 90)]
+
+    sel = lambda: rettn.rt_select_blocks(sh, q0, k0, forced, idx, None, ws)
+    cal = lambda: rettn.rt_calibrate(sh, q0, k0, v0, idx, cache, 0, out)
+    spa = lambda: rettn.rt_sparse_attn_reshape(sh, q1, k1, v1, None, cache, 0, out)
+    for fn in (sel, cal, spa):
+        fn()
+    torch.cuda.synchronize()
+    t_sel, _ = timed(sel, reps)
+    t_cal, _ = timed(cal, max(3, reps // 4))
+    t_warm, pw = timed(spa, reps)
+    t_cold, pc = timed(spa, reps, cold=True)
+    lists = idx.cpu().numpy()
+    flop = kept_flops(lists, N, d)
+    byts = sparse_call_bytes(lists, N, D, ebytes)
+    dense = 4 * d * N * N * sh.B * sh.H
+    sel_bytes = 2 * sh.B * sh.H * N * D * ebytes  # Q and K read once
+    res = {
+        "config": cfg["name"] if "name" in cfg else None,
+        "select_ms": round(t_sel, 4), "select_hbm_gbs": round(sel_bytes / (t_sel * 1e-3) / 1e9, 1),
+        "calibrate_ms": round(t_cal, 4), "calibrate_tflops": round(dense / (t_cal * 1e-3) / 1e12, 1),
+        "calibrate_mfma_frac": round(dense / (t_cal * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "sparse_warm_ms": round(t_warm, 5), "sparse_warm_p10_p50_p90": pw,
+        "sparse_cold_ms": round(t_cold, 5), "sparse_cold_p10_p50_p90": pc,
+        "sparse_kept_tflops_warm": round(flop / (t_warm * 1e-3) / 1e12, 1),
+        "sparse_mfma_frac_warm": round(flop / (t_warm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "sparse_alg_bytes": byts, "sparse_hbm_gbs_warm": round(byts / (t_warm * 1e-3) / 1e9, 1),
+        "stats_residual_gbs_warm": round((sh.B * sh.H * N * (D * 4 + 12)) / (t_warm * 1e-3) / 1e9, 1),
+        "kept_flop": flop, "dense_flop": dense,
+    }
+    cache.close()
+    return res
+
+
 def _cpu_model():
     try:
         for ln in open("/proc/cpuinfo"):
@@ -138,6 +215,12 @@ def main():
     import torch
     from sparse_attention_diffusion_amd import configs, rettn, synth
 
+    if args.all_configs:
+        torch.cuda.set_device(0)
+        for name in configs.CONFIGS:
+            c = dict(configs.CONFIGS[name], name=name)
+            print(json.dumps(components(c)), flush=True)
+        return
     cfg = dict(configs.CONFIGS[args.config])
     if args.denoise_steps:
         cfg["steps"] = args.denoise_steps
@@ -233,6 +316,11 @@ def main():
         "pages_context": {"kept_fraction": round(keep / configs.n_blocks(N), 4),
                           "skipped_fraction": round(1 - flop / (4 * d * N * N * cfg["B"] * cfg["H"]), 4)},
     }
+    del inputs
+    cache.close()
+    torch.cuda.empty_cache()
+    if not args.no_components:
+        res["components"] = components(dict(cfg, name=args.config))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads, args.cpu_budget_s)
     print(json.dumps(res), flush=True)
