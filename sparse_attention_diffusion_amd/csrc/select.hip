@@ -8,36 +8,97 @@
 // plus the best remaining ones (ties to the lower block index).
 //
 // Kernels
-//   pool_kernel   : one wave per (tensor, bh, block); float32 sums in token order.
-//   select_kernel : one wave per (bh, query block); float32 scores, then a
-//                   bitonic sort of (score, index) keys in LDS and an ascending
-//                   compaction of the winners with wave ballots.
+//   pool_kernel   : one wave per (tensor, bh, block).  The block's rows are
+//                   read as 16-byte chunks, all at once (HBM-bound: Q and K
+//                   are read once); float32 partial sums per row group are
+//                   reduced through LDS.  K means are written transposed
+//                   ([bh][d][block]) so that scoring reads them coalesced.
+//   select_kernel : one wave per (bh, QG query blocks).  Lane j scores key
+//                   blocks j, j+64, ... against the QG pooled queries (float32
+//                   dot products in ascending d), then each query block's
+//                   keep - n_forced winners are taken by rounds of a wave-wide
+//                   maximum of 64-bit (score, ~index) keys, and the list is
+//                   written in ascending order through a flag row and ballots.
+//                   Large selections fall back to a bitonic sort in LDS.
 #include "internal.h"
 
 namespace rettn {
 namespace {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte chunk of T elements, widened to float32.
 template <typename T>
-__device__ __forceinline__ float to_f32(T x);
+struct Chunk;
 template <>
-__device__ __forceinline__ float to_f32<float>(float x) { return x; }
+struct Chunk<float> {
+  static constexpr int E = 4;
+  __device__ static void widen(u32x4 c, float (&f)[8]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(c[e]);
+  }
+};
 template <>
-__device__ __forceinline__ float to_f32<__bf16>(__bf16 x) { return (float)x; }
+struct Chunk<__bf16> {
+  static constexpr int E = 8;
+  __device__ static void widen(u32x4 c, float (&f)[8]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = __uint_as_float(c[e] << 16);
+      f[2 * e + 1] = __uint_as_float(c[e] & 0xFFFF0000u);
+    }
+  }
+};
 
 // grid.x: (bh, block) pairs laid out per XCD; grid.y: 0 = q, 1 = k.
 template <typename T, int D>
 __global__ void __launch_bounds__(64) pool_kernel(SelectArgs a, XcdGrid grid) {
+  constexpr int E = Chunk<T>::E;          // elements per 16-byte chunk
+  constexpr int CPR = D / E;              // chunks per row
+  constexpr int RPI = 64 / CPR;           // rows per pass of the wave
+  constexpr int PASSES = (kBlock + RPI - 1) / RPI;
+  static_assert(D % E == 0 && CPR <= 64, "row chunks");
+  __shared__ float part[RPI][D];
+
   const uint32_t lin = grid.linear(blockIdx.x);
   if (lin >= grid.total) return;
   const int Nb = a.Nb, N = a.N;
   const int bh = lin / Nb, i = lin % Nb;
-  const T* x = (const T*)(blockIdx.y == 0 ? a.q : a.k) + (size_t)bh * N * D;
-  float* out = (blockIdx.y == 0 ? a.qb : a.kb) + ((size_t)bh * Nb + i) * D;
-  const int r0 = i * kBlock, r1 = min(N, r0 + kBlock);
-  for (int d = threadIdx.x; d < D; d += 64) {
-    float acc = 0.f;
-    for (int r = r0; r < r1; ++r) acc += to_f32<T>(x[(size_t)r * D + d]);
-    out[d] = acc / (float)(r1 - r0);
+  const bool isk = blockIdx.y != 0;
+  const int lane = threadIdx.x;
+  const int rg = lane / CPR, ch = lane % CPR;  // row in the pass, chunk in the row
+  const int r0 = i * kBlock, rows = min(N - r0, kBlock);
+  const char* base = (const char*)((const T*)(isk ? a.k : a.q) + ((size_t)bh * N + r0) * D);
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  if (rg < RPI) {
+    u32x4 c[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int r = p * RPI + rg;
+      c[p] = r < rows ? __builtin_nontemporal_load((const u32x4*)(base + ((size_t)r * D + ch * E) * sizeof(T)))
+                      : u32x4{};
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      float f[8];
+      Chunk<T>::widen(c[p], f);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += f[e];
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) part[rg][ch * E + e] = acc[e];
+  }
+  __syncthreads();
+  const float inv = 1.f / (float)rows;
+  for (int d = lane; d < D; d += 64) {
+    float s = 0.f;
+#pragma unroll
+    for (int g = 0; g < RPI; ++g) s += part[g][d];
+    if (isk) a.kb[((size_t)bh * D + d) * Nb + i] = s * inv;  // transposed
+    else a.qb[((size_t)bh * Nb + i) * D + d] = s * inv;
   }
 }
 
@@ -47,63 +108,22 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-template <int D>
-__global__ void __launch_bounds__(64) select_kernel(SelectArgs a, XcdGrid grid) {
-  __shared__ unsigned long long keys[kMaxBlocks];
-  __shared__ float qrow[D];
-  __shared__ unsigned char flags[kMaxBlocks];
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned lo = __shfl_xor((unsigned)x, o), hi = __shfl_xor((unsigned)(x >> 32), o);
+    const unsigned long long y = ((unsigned long long)hi << 32) | lo;
+    x = y > x ? y : x;
+  }
+  return x;
+}
 
-  const uint32_t lin = grid.linear(blockIdx.x);
-  if (lin >= grid.total) return;
-  const int Nb = a.Nb, keep = a.keep;
-  const int bh = lin / Nb, i = lin % Nb;
+constexpr int kQG = 4;          // query blocks per wave
+constexpr int kMaxRounds = 32;  // above this many non-forced winners: bitonic sort
+
+// Writes the kept list of one query block from its flag row (ascending).
+__device__ __forceinline__ void emit(const unsigned char* flags, int Nb, int32_t* out) {
   const int lane = threadIdx.x;
-  const float* kb = a.kb + (size_t)bh * Nb * D;
-  for (int d = lane; d < D; d += 64) qrow[d] = a.qb[((size_t)bh * Nb + i) * D + d];
-  int P = 64;
-  while (P < Nb) P <<= 1;
-  __syncthreads();
-
-  float* srow = a.scores ? a.scores + ((size_t)bh * Nb + i) * Nb : nullptr;
-  for (int j = lane; j < P; j += 64) {
-    unsigned long long key = 0ull;  // padding sorts last
-    if (j < Nb) {
-      float acc = 0.f;
-      const float* kr = kb + (size_t)j * D;
-#pragma unroll 8
-      for (int d = 0; d < D; ++d) acc = fmaf(qrow[d], kr[d], acc);
-      float s = acc * a.alpha + 0.0f;  // + 0 turns -0 into +0: equal scores compare equal
-      if (srow) srow[j] = s;
-      const bool forced = (a.forced[j >> 5] >> (j & 31)) & 1u;
-      const uint32_t hi = forced ? 0xFFFFFFFFu : order_key(s);
-      key = ((unsigned long long)hi << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)j);
-    }
-    keys[j] = key;
-  }
-  __syncthreads();
-
-  // Bitonic sort of P keys, descending.
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int t = lane; t < (P >> 1); t += 64) {
-        const int lo = (t / j) * 2 * j + (t % j);
-        const int hi = lo + j;
-        const unsigned long long x = keys[lo], y = keys[hi];
-        const bool desc = (lo & k) == 0;
-        if ((x < y) == desc) {
-          keys[lo] = y;
-          keys[hi] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
-
-  for (int j = lane; j < Nb; j += 64) flags[j] = 0;
-  __syncthreads();
-  for (int t = lane; t < keep; t += 64) flags[0xFFFFFFFFu - (uint32_t)(keys[t] & 0xFFFFFFFFull)] = 1;
-  __syncthreads();
-  int32_t* out = a.idx + ((size_t)bh * Nb + i) * keep;
   int cnt = 0;
   for (int base = 0; base < Nb; base += 64) {
     const int j = base + lane;
@@ -114,13 +134,140 @@ __global__ void __launch_bounds__(64) select_kernel(SelectArgs a, XcdGrid grid) 
   }
 }
 
+// CH: key blocks per lane (64-block chunks), at least ceil(Nb / 64).
+template <int D, int CH>
+__global__ void __launch_bounds__(64) select_kernel(SelectArgs a, XcdGrid grid) {
+  __shared__ __attribute__((aligned(16))) float qrow[kQG][D];
+  __shared__ unsigned char flags[kQG][kMaxBlocks];
+  __shared__ unsigned long long keys[kMaxBlocks];
+
+  const uint32_t lin = grid.linear(blockIdx.x);
+  if (lin >= grid.total) return;
+  const int Nb = a.Nb, keep = a.keep;
+  const int groups = (Nb + kQG - 1) / kQG;
+  const int bh = lin / groups, i0 = (lin % groups) * kQG;
+  const int nq = min(kQG, Nb - i0);
+  const int lane = threadIdx.x;
+  for (int e = lane; e < kQG * D; e += 64) {
+    const int g = e / D, d = e % D;
+    qrow[g][d] = g < nq ? a.qb[((size_t)bh * Nb + i0 + g) * D + d] : 0.f;
+  }
+  for (int e = lane; e < kQG * kMaxBlocks; e += 64) (&flags[0][0])[e] = 0;
+  int n_forced = 0;
+#pragma unroll
+  for (int w = 0; w < kMaxBlocks / 32; ++w) n_forced += __popc(a.forced[w]);
+  __syncthreads();
+
+  // Scores of key blocks j = lane + 64c against the kQG pooled queries.
+  const float* kt = a.kb + (size_t)bh * D * Nb;  // transposed means [d][j]
+  const int nc = (Nb + 63) / 64;
+  float sc[kQG][CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    if (c < nc) {
+      const int j = c * 64 + lane;
+      const int jj = min(j, Nb - 1);
+      float acc[kQG];
+#pragma unroll
+      for (int g = 0; g < kQG; ++g) acc[g] = 0.f;
+      for (int d = 0; d < D; d += 4) {
+        float kv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kv[e] = kt[(size_t)(d + e) * Nb + jj];
+#pragma unroll
+        for (int g = 0; g < kQG; ++g) {
+          const f32x4 qv = *(const f32x4*)&qrow[g][d];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[g] = fmaf(qv[e], kv[e], acc[g]);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < kQG; ++g) sc[g][c] = acc[g] * a.alpha + 0.0f;  // + 0: -0 -> +0
+    }
+  }
+
+#pragma unroll
+  for (int g = 0; g < kQG; ++g) {
+    if (g >= nq) break;
+    const int i = i0 + g;
+    if (a.scores) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int j = c * 64 + lane;
+        if (c < nc && j < Nb) a.scores[((size_t)bh * Nb + i) * Nb + j] = sc[g][c];
+      }
+    }
+    // 64-bit keys: order-preserving score bits, then ~j (ties to the lower j);
+    // forced blocks are marked directly and take no round.
+    unsigned long long kk[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int j = c * 64 + lane;
+      kk[c] = 0ull;
+      if (c < nc && j < Nb) {
+        if ((a.forced[j >> 5] >> (j & 31)) & 1u) flags[g][j] = 1;
+        else kk[c] = ((unsigned long long)order_key(sc[g][c]) << 32) | (0xFFFFFFFFu - (uint32_t)j);
+      }
+    }
+    const int rounds = keep - n_forced;
+    if (rounds <= kMaxRounds) {
+      for (int t = 0; t < rounds; ++t) {
+        unsigned long long best = 0ull;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) best = kk[c] > best ? kk[c] : best;
+        best = wave_max_u64(best);
+        if (best == 0ull) break;  // no candidate left (more rounds than blocks)
+        const int jw = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+        if (lane == (jw & 63)) {
+          flags[g][jw] = 1;
+#pragma unroll
+          for (int c = 0; c < CH; ++c)
+            if (c == (jw >> 6)) kk[c] = 0ull;
+        }
+      }
+    } else {
+      // Bitonic sort of the non-forced keys, descending.
+      int P = 64;
+      while (P < Nb) P <<= 1;
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        if (c * 64 < P) keys[c * 64 + lane] = kk[c];
+      __syncthreads();
+      for (int k = 2; k <= P; k <<= 1) {
+        for (int jx = k >> 1; jx > 0; jx >>= 1) {
+          for (int t = lane; t < (P >> 1); t += 64) {
+            const int lo = (t / jx) * 2 * jx + (t % jx);
+            const int hi = lo + jx;
+            const unsigned long long x = keys[lo], y = keys[hi];
+            const bool desc = (lo & k) == 0;
+            if ((x < y) == desc) {
+              keys[lo] = y;
+              keys[hi] = x;
+            }
+          }
+          __syncthreads();
+        }
+      }
+      for (int t = lane; t < rounds; t += 64) flags[g][0xFFFFFFFFu - (uint32_t)(keys[t] & 0xFFFFFFFFull)] = 1;
+    }
+    __syncthreads();
+    emit(flags[g], Nb, a.idx + ((size_t)bh * Nb + i) * keep);
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_typed(const SelectArgs& a, hipStream_t s) {
-  XcdGrid grid = make_xcd_grid((uint32_t)a.BH * (uint32_t)a.Nb);
-  hipLaunchKernelGGL((pool_kernel<T, D>), dim3(grid.grid(), 2), dim3(64), 0, s, a, grid);
+  XcdGrid pg = make_xcd_grid((uint32_t)a.BH * (uint32_t)a.Nb);
+  hipLaunchKernelGGL((pool_kernel<T, D>), dim3(pg.grid(), 2), dim3(64), 0, s, a, pg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((select_kernel<D>), dim3(grid.grid()), dim3(64), 0, s, a, grid);
+  XcdGrid sg = make_xcd_grid((uint32_t)a.BH * (uint32_t)((a.Nb + kQG - 1) / kQG));
+  const int nc = (a.Nb + 63) / 64;
+  if (nc <= 1) hipLaunchKernelGGL((select_kernel<D, 1>), dim3(sg.grid()), dim3(64), 0, s, a, sg);
+  else if (nc <= 2) hipLaunchKernelGGL((select_kernel<D, 2>), dim3(sg.grid()), dim3(64), 0, s, a, sg);
+  else if (nc <= 4) hipLaunchKernelGGL((select_kernel<D, 4>), dim3(sg.grid()), dim3(64), 0, s, a, sg);
+  else if (nc <= 8) hipLaunchKernelGGL((select_kernel<D, 8>), dim3(sg.grid()), dim3(64), 0, s, a, sg);
+  else hipLaunchKernelGGL((select_kernel<D, kMaxBlocks / 64>), dim3(sg.grid()), dim3(64), 0, s, a, sg);
   return hipGetLastError();
 }
 
