@@ -173,6 +173,17 @@ def components(cfg, reps=20, flush_mb=512):
     t_cal, _ = timed(cal, max(3, reps // 4))
     t_warm, pw = timed(spa, reps)
     t_cold, pc = timed(spa, reps, cold=True)
+    # the same with the residual cached in bf16 (cache option; float32 is the baseline)
+    t16w = t16c = None
+    if cfg["dtype"] == "bf16":
+        c16 = rettn.StatsCache(sh, 1, device=dev, residual="bf16")
+        rettn.rt_calibrate(sh, q0, k0, v0, idx, c16, 0, out)
+        spa16 = lambda: rettn.rt_sparse_attn_reshape(sh, q1, k1, v1, None, c16, 0, out)
+        spa16()
+        torch.cuda.synchronize()
+        t16w, _ = timed(spa16, reps)
+        t16c, _ = timed(spa16, reps, cold=True)
+        c16.close()
     lists = idx.cpu().numpy()
     flop = kept_flops(lists, N, d)
     byts = sparse_call_bytes(lists, N, D, ebytes)
@@ -190,6 +201,9 @@ def components(cfg, reps=20, flush_mb=512):
         "sparse_alg_bytes": byts, "sparse_hbm_gbs_warm": round(byts / (t_warm * 1e-3) / 1e9, 1),
         "stats_residual_gbs_warm": round((sh.B * sh.H * N * (D * 4 + 12)) / (t_warm * 1e-3) / 1e9, 1),
         "kept_flop": flop, "dense_flop": dense,
+        "sparse_bf16_residual_warm_ms": None if t16w is None else round(t16w, 5),
+        "sparse_bf16_residual_cold_ms": None if t16c is None else round(t16c, 5),
+        "sparse_bf16_residual_alg_bytes": None if t16w is None else byts - sh.B * sh.H * N * D * 2,
     }
     cache.close()
     return res

@@ -89,7 +89,8 @@ typedef struct rt_stats_cache rt_stats_cache;
 
 /* Device pointers of one layer of the statistics cache.
  *   m, z_full, z_sparse : float32 [B, H, N]
- *   R                   : float32 [B, H, N, d_pad], row-major
+ *   R                   : [B, H, N, d_pad], row-major; float32 by default, bf16
+ *                         (reinterpret the pointer) when r_dtype == RT_BF16
  *   idx                 : int32   [B, H, Nb, keep], each row ascending
  * `valid` is 1 once the layer has been calibrated (or marked valid).       */
 typedef struct {
@@ -100,6 +101,7 @@ typedef struct {
   int32_t* idx;
   int64_t rows;      /* B*H*N */
   int32_t valid;
+  int32_t r_dtype;   /* rt_dtype of R */
 } rt_stats_view;
 
 const char* rt_status_string(int32_t status);
@@ -135,6 +137,15 @@ rt_status rt_select_blocks(const rt_shape* shape, const void* q, const void* k,
 size_t rt_stats_cache_bytes(const rt_shape* shape, int32_t n_layers);
 rt_status rt_stats_cache_init(rt_stats_cache** out, const rt_shape* shape, int32_t n_layers,
                               void* dev_mem, size_t bytes);
+/* The same with the residual's storage type chosen: RT_F32 (what the two calls
+ * above use) or RT_BF16, which halves the residual's bytes (the largest part of
+ * the cache and of a sparse call's traffic) at the cost of rounding R to bf16
+ * (relative error <= 2^-9 per element).  RT_BF16 requires shape->dtype ==
+ * RT_BF16 (RT_E_DTYPE otherwise); any other value is RT_E_DTYPE (init) or 0
+ * bytes.  The calibration kernel rounds the float32 residual to nearest even. */
+size_t rt_stats_cache_bytes_ex(const rt_shape* shape, int32_t n_layers, int32_t residual_dtype);
+rt_status rt_stats_cache_init_ex(rt_stats_cache** out, const rt_shape* shape, int32_t n_layers,
+                                 int32_t residual_dtype, void* dev_mem, size_t bytes);
 rt_status rt_stats_cache_view(const rt_stats_cache* cache, int32_t layer, rt_stats_view* out);
 rt_status rt_stats_cache_set_valid(rt_stats_cache* cache, int32_t layer, int32_t valid);
 rt_status rt_stats_cache_invalidate(rt_stats_cache* cache, int32_t layer);

@@ -25,6 +25,7 @@ struct rt_stats_cache {
   char* base;
   size_t bytes;
   size_t off_m, off_zf, off_zs, off_R, off_idx, layer_stride;
+  int32_t r_dtype;  // rt_dtype of the residual
   std::vector<int32_t> valid;
 };
 
@@ -119,7 +120,7 @@ void layout(rt_stats_cache* c) {
   c->off_m = off; off += align_up(rows * 4);
   c->off_zf = off; off += align_up(rows * 4);
   c->off_zs = off; off += align_up(rows * 4);
-  c->off_R = off; off += align_up(rows * s.d_pad * 4);
+  c->off_R = off; off += align_up(rows * s.d_pad * (c->r_dtype == RT_BF16 ? 2 : 4));
   c->off_idx = off; off += align_up(lists * 4);
   c->layer_stride = off;
 }
@@ -135,6 +136,7 @@ AttnArgs attn_args(const rt_shape* s, const void* q, const void* k, const void* 
   a.z_full = (float*)(base + c->off_zf);
   a.z_sparse = (float*)(base + c->off_zs);
   a.R = (float*)(base + c->off_R);
+  a.r_bf16 = c->r_dtype == RT_BF16 ? 1 : 0;
   a.BH = s->B * s->H;
   a.N = s->N;
   a.Nb = (int32_t)nblocks(s->N);
@@ -234,22 +236,37 @@ rt_status rt_select_blocks(const rt_shape* s, const void* q, const void* k, cons
   return launched(rettn::launch_select(s->dtype == RT_BF16, s->d_pad, a, hs), hs, "rt_select_blocks");
 }
 
-size_t rt_stats_cache_bytes(const rt_shape* s, int32_t n_layers) {
+size_t rt_stats_cache_bytes_ex(const rt_shape* s, int32_t n_layers, int32_t residual_dtype) {
   if (check_shape(s) != RT_OK || n_layers < 1) return 0;
+  if (residual_dtype != RT_F32 && !(residual_dtype == RT_BF16 && s->dtype == RT_BF16)) return 0;
   rt_stats_cache c{};
   c.shape = *s;
+  c.r_dtype = residual_dtype;
   layout(&c);
   return c.layer_stride * (size_t)n_layers;
 }
 
+size_t rt_stats_cache_bytes(const rt_shape* s, int32_t n_layers) {
+  return rt_stats_cache_bytes_ex(s, n_layers, RT_F32);
+}
+
 rt_status rt_stats_cache_init(rt_stats_cache** out, const rt_shape* s, int32_t n_layers, void* dev_mem,
                               size_t bytes) {
+  return rt_stats_cache_init_ex(out, s, n_layers, RT_F32, dev_mem, bytes);
+}
+
+rt_status rt_stats_cache_init_ex(rt_stats_cache** out, const rt_shape* s, int32_t n_layers, int32_t residual_dtype,
+                                 void* dev_mem, size_t bytes) {
   if (out == nullptr) return fail(RT_E_ARG, "out is NULL");
   *out = nullptr;
   rt_status st = check_shape(s);
   if (st != RT_OK) return st;
   if (n_layers < 1) return fail(RT_E_ARG, "n_layers must be >= 1 (got %d)", n_layers);
-  const size_t need = rt_stats_cache_bytes(s, n_layers);
+  if (residual_dtype != RT_F32 && residual_dtype != RT_BF16)
+    return fail(RT_E_DTYPE, "residual dtype %d is not RT_F32 or RT_BF16", residual_dtype);
+  if (residual_dtype == RT_BF16 && s->dtype != RT_BF16)
+    return fail(RT_E_DTYPE, "a bf16 residual needs bf16 q/k/v (shape dtype %d)", s->dtype);
+  const size_t need = rt_stats_cache_bytes_ex(s, n_layers, residual_dtype);
   if (need > 0 && dev_mem == nullptr && !is_empty(s)) return fail(RT_E_ARG, "dev_mem is NULL");
   if (dev_mem != nullptr && (reinterpret_cast<uintptr_t>(dev_mem) % kAlign) != 0)
     return fail(RT_E_ARG, "dev_mem must be %zu-byte aligned", kAlign);
@@ -257,6 +274,7 @@ rt_status rt_stats_cache_init(rt_stats_cache** out, const rt_shape* s, int32_t n
   rt_stats_cache* c = new (std::nothrow) rt_stats_cache();
   if (c == nullptr) return fail(RT_E_ARG, "host allocation failed");
   c->shape = *s;
+  c->r_dtype = residual_dtype;
   c->n_layers = n_layers;
   c->base = (char*)dev_mem;
   c->bytes = bytes;
@@ -277,6 +295,7 @@ rt_status rt_stats_cache_view(const rt_stats_cache* c, int32_t layer, rt_stats_v
   out->idx = (int32_t*)(base + c->off_idx);
   out->rows = (int64_t)c->shape.B * c->shape.H * c->shape.N;
   out->valid = c->valid[layer];
+  out->r_dtype = c->r_dtype;
   return RT_OK;
 }
 

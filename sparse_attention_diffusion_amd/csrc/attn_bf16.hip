@@ -485,13 +485,14 @@ struct PipeStats {
   float mc, zf, zs;
 };
 
-template <int D>
+template <int D, bool RB>
 __device__ __forceinline__ void pipe_load(bf16x8 (&q)[Shape<D>::KS], PipeStats<D>& st, f32x4 (&r)[Shape<D>::NT][4],
                                           const AttnArgs& a, int bh, int qi, int rowq, int g) {
   const size_t r0 = (size_t)bh * a.N + (size_t)qi * kBlock;  // first row of the block
   const int rows = min(a.N - qi * kBlock, kBlock);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)a.q + r0 * D * 2, rows * D * 2);
-  const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.R + r0 * D, rows * D * 4);
+  const __amdgpu_buffer_rsrc_t rr =
+      RB ? make_rsrc((const __bf16*)a.R + r0 * D, rows * D * 2) : make_rsrc(a.R + r0 * D, rows * D * 4);
 #pragma unroll
   for (int ks = 0; ks < Shape<D>::KS; ++ks)
     q[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, (rowq * D + 16 * ks + 8 * g) * 2, 0, 0));
@@ -504,11 +505,17 @@ __device__ __forceinline__ void pipe_load(bf16x8 (&q)[Shape<D>::KS], PipeStats<D
   for (int t = 0; t < Shape<D>::NT; ++t)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      if (32 * t + 8 * i4 < D)
+      if (32 * t + 8 * i4 >= D) {
+        r[t][i4] = f32x4{};
+      } else if (RB) {  // four bf16, widened exactly
+        const u32x2 h = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rr, (rowq * D + 32 * t + 8 * i4 + 4 * g) * 2, 0, 0));
+        r[t][i4] = f32x4{__uint_as_float(h[0] << 16), __uint_as_float(h[0] & 0xFFFF0000u),
+                         __uint_as_float(h[1] << 16), __uint_as_float(h[1] & 0xFFFF0000u)};
+      } else {
         r[t][i4] = __builtin_bit_cast(
             f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, (rowq * D + 32 * t + 8 * i4 + 4 * g) * 4, 0, 0));
-      else
-        r[t][i4] = f32x4{};
+      }
     }
 }
 
@@ -552,7 +559,7 @@ __device__ __forceinline__ void probs_ref(bf16x8 (&p)[2][2], const f32x16 (&s)[2
 // O = acc * Z_sparse / (Z * Z_full) with Z the kept mass.  All global traffic
 // goes through buffer resources whose byte limit zero-fills rows past N on
 // loads and drops them on stores.
-template <int D>
+template <int D, bool RB>
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 3, 4)))
 sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
   constexpr int NT = Shape<D>::NT, KS = Shape<D>::KS, TILE = Shape<D>::TILE, ROW = Shape<D>::ROW;
@@ -618,7 +625,7 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
   // `it`: NLD loads.
   auto load_rows = [&]() {
     f32x4 r[NT][4];
-    pipe_load<D>(q, st, r, a, it.bh, it.qi, rowq, g);
+    pipe_load<D, RB>(q, st, r, a, it.bh, it.qi, rowq, g);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -717,6 +724,13 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
   }
 }
 
+// Both residual types of the sparse kernel, instantiated explicitly (the host
+// compiler otherwise emits the launch stub of only one of them).
+template __global__ void sparse_occ_kernel<64, false>(AttnArgs, PersistGrid);
+template __global__ void sparse_occ_kernel<64, true>(AttnArgs, PersistGrid);
+template __global__ void sparse_occ_kernel<80, false>(AttnArgs, PersistGrid);
+template __global__ void sparse_occ_kernel<80, true>(AttnArgs, PersistGrid);
+
 // ---------------------------------------------------------------- calibration step
 template <int D, int NBUF, int QB>
 struct CalibCtx {
@@ -770,7 +784,7 @@ struct CalibCtx {
   }
 };
 
-template <int D, int NBUF, int QB>
+template <int D, int NBUF, int QB, bool RB>
 __global__ void __launch_bounds__(128 * QB) calib_kernel(AttnArgs a, XcdGrid grid) {
   constexpr int NT = Shape<D>::NT;
   static_assert(NBUF >= 2 && NBUF <= 3, "ring depth");
@@ -842,7 +856,6 @@ __global__ void __launch_bounds__(128 * QB) calib_kernel(AttnArgs a, XcdGrid gri
       a.z_sparse[srow] = zs;
     }
     const float inv = 1.f / zf;
-    float* rrow = a.R + srow * D;
     __bf16* orow = (__bf16*)a.o + srow * D;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -857,7 +870,14 @@ __global__ void __launch_bounds__(128 * QB) calib_kernel(AttnArgs a, XcdGrid gri
             r[e] = cx.ores[t][4 * i4 + e] * f;
             ob[e] = (__bf16)((cx.okept[t][4 * i4 + e] * f + r[e]) * inv);
           }
-          *(f32x4*)(rrow + d) = r;
+          if (RB) {  // residual rounded to bf16 (nearest even)
+            __bf16 rb[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rb[e] = (__bf16)r[e];
+            *(u32x2*)((__bf16*)a.R + srow * D + d) = *(u32x2*)rb;
+          } else {
+            *(f32x4*)(a.R + srow * D + d) = r;
+          }
           *(u32x2*)(orow + d) = *(u32x2*)ob;
         }
       }
@@ -876,12 +896,19 @@ hipError_t launch_d(AttnMode mode, const AttnArgs& a, hipStream_t s) {
     const uint32_t total = (uint32_t)a.BH * (uint32_t)a.Nb;
     PersistGrid pg{total, (total + 7u) / 8u, 0u};
     pg.g = min(pg.per, (uint32_t)(D == 64 ? kSparseWgPerXcd64 : kSparseWgPerXcd80));
-    hipLaunchKernelGGL((sparse_occ_kernel<D>), dim3(8u * pg.g), dim3(128), 0, s, a, pg);
+    if (a.r_bf16) {
+      hipLaunchKernelGGL((sparse_occ_kernel<D, true>), dim3(8u * pg.g), dim3(128), 0, s, a, pg);
+    } else {
+      hipLaunchKernelGGL((sparse_occ_kernel<D, false>), dim3(8u * pg.g), dim3(128), 0, s, a, pg);
+    }
   } else {
     constexpr int QB = 2;  // 2*QB waves must divide the LDS row units; 2 workgroups per CU
     const uint32_t groups = (uint32_t)(a.Nb + QB - 1) / QB;
     XcdGrid grid = make_xcd_grid((uint32_t)a.BH * groups);
-    hipLaunchKernelGGL((calib_kernel<D, kCalibRing, QB>), dim3(grid.grid()), dim3(128 * QB), 0, s, a, grid);
+    if (a.r_bf16)
+      hipLaunchKernelGGL((calib_kernel<D, kCalibRing, QB, true>), dim3(grid.grid()), dim3(128 * QB), 0, s, a, grid);
+    else
+      hipLaunchKernelGGL((calib_kernel<D, kCalibRing, QB, false>), dim3(grid.grid()), dim3(128 * QB), 0, s, a, grid);
   }
   return hipGetLastError();
 }

@@ -21,9 +21,10 @@ struct AttnArgs {
   float* m;                // statistics cache rows [BH, N]
   float* z_full;
   float* z_sparse;
-  float* R;                // [BH, N, D]
+  float* R;                // [BH, N, D]: float32, or bf16 when r_bf16
   int32_t BH, N, Nb, keep;
   float alpha;             // 1/sqrt(d)
+  int32_t r_bf16;          // residual stored as bf16 (bf16 kernels only)
 };
 
 struct SelectArgs {

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(_HERE, "_lib", "librettn.so")
 
 RT_OK, RT_E_ARG, RT_E_SHAPE, RT_E_DTYPE, RT_E_STATE, RT_E_WORKSPACE, RT_E_LAUNCH, RT_E_DEVICE = range(8)
 RT_BF16, RT_F32 = 0, 1
+_DTYPES = {"bf16": RT_BF16, "f32": RT_F32}
 BLOCK = 64
 
 
@@ -24,7 +25,7 @@ class RtShape(ctypes.Structure):
 class RtStatsView(ctypes.Structure):
     _fields_ = [("m", ctypes.c_void_p), ("z_full", ctypes.c_void_p), ("z_sparse", ctypes.c_void_p),
                 ("R", ctypes.c_void_p), ("idx", ctypes.c_void_p), ("rows", ctypes.c_int64),
-                ("valid", ctypes.c_int32)]
+                ("valid", ctypes.c_int32), ("r_dtype", ctypes.c_int32)]
 
 
 class RettnError(RuntimeError):
@@ -47,6 +48,8 @@ def _load():
         "rt_select_blocks": (I32, [S, P, P, ctypes.POINTER(I32), I32, P, P, P, SZ, P]),
         "rt_stats_cache_bytes": (SZ, [S, I32]),
         "rt_stats_cache_init": (I32, [ctypes.POINTER(P), S, I32, P, SZ]),
+        "rt_stats_cache_bytes_ex": (SZ, [S, I32, I32]),
+        "rt_stats_cache_init_ex": (I32, [ctypes.POINTER(P), S, I32, I32, P, SZ]),
         "rt_stats_cache_view": (I32, [P, I32, ctypes.POINTER(RtStatsView)]),
         "rt_stats_cache_set_valid": (I32, [P, I32, I32]),
         "rt_stats_cache_invalidate": (I32, [P, I32]),
@@ -68,7 +71,8 @@ def _load():
 _lib = _load()
 SYMBOLS = [
     "rt_status_string", "rt_last_error", "rt_version", "rt_num_blocks", "rt_select_workspace_bytes",
-    "rt_select_blocks", "rt_stats_cache_bytes", "rt_stats_cache_init", "rt_stats_cache_view",
+    "rt_select_blocks", "rt_stats_cache_bytes", "rt_stats_cache_init", "rt_stats_cache_bytes_ex",
+    "rt_stats_cache_init_ex", "rt_stats_cache_view",
     "rt_stats_cache_set_valid", "rt_stats_cache_invalidate", "rt_stats_cache_destroy", "rt_calibrate",
     "rt_sparse_attn_reshape", "rt_schedule_is_calibration", "rt_step_workspace_bytes", "rt_attention_step",
 ]
@@ -124,6 +128,10 @@ def stats_cache_bytes(sh, n_layers=1):
     return _lib.rt_stats_cache_bytes(ctypes.byref(sh), n_layers)
 
 
+def stats_cache_bytes_ex(sh, n_layers=1, residual="f32"):
+    return _lib.rt_stats_cache_bytes_ex(ctypes.byref(sh), n_layers, _DTYPES[residual])
+
+
 def schedule_is_calibration(step, period):
     return bool(_lib.rt_schedule_is_calibration(step, period))
 
@@ -145,16 +153,18 @@ def rt_select_blocks(sh, q, k, forced, block_idx, pooled_scores, workspace, stre
 class StatsCache:
     """Host handle plus the device memory (a torch byte tensor) it wraps."""
 
-    def __init__(self, sh, n_layers=1, device="cuda", memory=None):
+    def __init__(self, sh, n_layers=1, device="cuda", memory=None, residual="f32"):
+        """residual: storage type of R, "f32" (default) or "bf16"."""
         self.shape = sh
         self.n_layers = n_layers
-        nbytes = stats_cache_bytes(sh, n_layers)
+        self.residual = residual
+        nbytes = stats_cache_bytes_ex(sh, n_layers, residual)
         if memory is None:
             memory = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
         self.memory = memory
         self.handle = ctypes.c_void_p()
-        _check(_lib.rt_stats_cache_init(ctypes.byref(self.handle), ctypes.byref(sh), n_layers,
-                                        _ptr(memory), memory.numel()))
+        _check(_lib.rt_stats_cache_init_ex(ctypes.byref(self.handle), ctypes.byref(sh), n_layers,
+                                           _DTYPES[residual], _ptr(memory), memory.numel()))
 
     def view(self, layer=0):
         v = RtStatsView()
@@ -178,7 +188,8 @@ class StatsCache:
             m=sub(v.m, rows, torch.float32, (sh.B, sh.H, sh.N)),
             z_full=sub(v.z_full, rows, torch.float32, (sh.B, sh.H, sh.N)),
             z_sparse=sub(v.z_sparse, rows, torch.float32, (sh.B, sh.H, sh.N)),
-            R=sub(v.R, rows * sh.d_pad, torch.float32, (sh.B, sh.H, sh.N, sh.d_pad)),
+            R=sub(v.R, rows * sh.d_pad, torch.bfloat16 if v.r_dtype == 0 else torch.float32,
+                  (sh.B, sh.H, sh.N, sh.d_pad)),
             idx=sub(v.idx, sh.B * sh.H * nb * sh.keep, torch.int32, (sh.B, sh.H, nb, sh.keep)),
             valid=v.valid,
         )

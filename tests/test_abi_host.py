@@ -104,6 +104,37 @@ def test_cache_layout_views():
     del buf
 
 
+def test_bf16_residual_cache_layout():
+    """A bf16 residual halves the R section and nothing else; it needs bf16 q/k/v."""
+    lib = rettn.lib()
+    sh = rettn.shape(2, 3, 1000, 64, 64, 5, dtype="bf16")
+    rows = 2 * 3 * 1000
+    f32 = rettn.stats_cache_bytes_ex(sh, 1, "f32")
+    b16 = rettn.stats_cache_bytes_ex(sh, 1, "bf16")
+    assert f32 == rettn.stats_cache_bytes(sh, 1)
+    assert f32 - b16 == rows * 64 * 2  # 256-B alignment of every section keeps the difference exact here
+    buf, addr = _fake_dev_memory(2 * b16)
+    h = ctypes.c_void_p()
+    assert lib.rt_stats_cache_init_ex(ctypes.byref(h), ctypes.byref(sh), 2, rettn.RT_BF16,
+                                      ctypes.c_void_p(addr), 2 * b16) == 0
+    v0, v1 = rettn.RtStatsView(), rettn.RtStatsView()
+    assert lib.rt_stats_cache_view(h, 0, ctypes.byref(v0)) == 0 and lib.rt_stats_cache_view(h, 1, ctypes.byref(v1)) == 0
+    assert v0.r_dtype == rettn.RT_BF16 and v1.m - v0.m == b16
+    assert v0.idx - v0.R >= rows * 64 * 2
+    assert lib.rt_stats_cache_destroy(h) == 0
+    # too little memory for a float32 residual
+    assert lib.rt_stats_cache_init_ex(ctypes.byref(h), ctypes.byref(sh), 1, rettn.RT_F32,
+                                      ctypes.c_void_p(addr), b16) == rettn.RT_E_WORKSPACE
+    # float32 inputs cannot have a bf16 residual; unknown residual types are refused
+    shf = rettn.shape(2, 3, 1000, 64, 64, 5, dtype="f32")
+    assert rettn.stats_cache_bytes_ex(shf, 1, "bf16") == 0
+    assert lib.rt_stats_cache_init_ex(ctypes.byref(h), ctypes.byref(shf), 1, rettn.RT_BF16,
+                                      ctypes.c_void_p(addr), 2 * b16) == rettn.RT_E_DTYPE
+    assert lib.rt_stats_cache_init_ex(ctypes.byref(h), ctypes.byref(sh), 1, 7,
+                                      ctypes.c_void_p(addr), 2 * b16) == rettn.RT_E_DTYPE
+    assert lib.rt_stats_cache_bytes_ex(ctypes.byref(sh), 1, 7) == 0
+
+
 def test_cache_init_errors():
     lib = rettn.lib()
     sh = rettn.shape(1, 2, 100, 64, 64, 2)

@@ -95,9 +95,16 @@ def test_selector_on_workload(name):
 
 
 # ------------------------------------------------------------------ attention
-def run_full_parity(cfg, steps_to_check, seed=0):
+def bf16_round(x):
+    """float64 array rounded to bf16 (nearest even) and back, on the CPU."""
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).double().numpy()
+
+
+def run_full_parity(cfg, steps_to_check, seed=0, residual="f32"):
     """Oracle lists fed to the GPU; calibrate at step 0, reshape at later steps;
-    the full layer is compared."""
+    the full layer is compared.  With a bf16 residual cache the later steps are
+    checked against the oracle fed its residual rounded to bf16 and against the
+    exact oracle, both to the same tolerance."""
     sh = rettn.shape_of(cfg)
     N, d = cfg["N"], cfg["d"]
     forced = configs.forced_blocks(cfg)
@@ -106,10 +113,11 @@ def run_full_parity(cfg, steps_to_check, seed=0):
     q0, k0, v0 = stepsin[0]
     ref_idx = gu.oracle_lists(cfg, q0, k0, forced, cfg["keep"])
     idx = torch.as_tensor(ref_idx).to(gu.DEV)
-    cache = rettn.StatsCache(sh, 1)
+    cache = rettn.StatsCache(sh, 1, residual=residual)
     o_cal = gu.calibrate(sh, q0, k0, v0, idx, cache)
     torch.cuda.synchronize()
     ref_cal = oracle.calibrate(gu.host(q0), gu.host(k0), gu.host(v0), ref_idx, N, d)
+    ref_cal_stored = dict(ref_cal, r=bf16_round(ref_cal["r"])) if residual == "bf16" else ref_cal
     tol = dict(max_rel=1e-5, l1_rel=1e-6) if cfg["dtype"] == "f32" else {}
     res = {"calibrate": gu.assert_close(gu.host(o_cal), ref_cal["o"], what="calibrate O", **tol)}
     t = cache.tensors(0)
@@ -126,6 +134,9 @@ def run_full_parity(cfg, steps_to_check, seed=0):
         torch.cuda.synchronize()
         ref_o = oracle.sparse_reshape(gu.host(q), gu.host(k), gu.host(v), ref_idx, ref_cal, N, d)
         res[f"step{s}"] = gu.assert_close(gu.host(o), ref_o, what=f"step {s} O", **tol)
+        if residual == "bf16":
+            ref_s = oracle.sparse_reshape(gu.host(q), gu.host(k), gu.host(v), ref_idx, ref_cal_stored, N, d)
+            res[f"step{s}_stored"] = gu.assert_close(gu.host(o), ref_s, what=f"step {s} O (rounded R)", **tol)
     cache.close()
     return res
 
@@ -145,7 +156,7 @@ def test_parity_pixart1024():
     run_full_parity(configs.CONFIGS["pixart1024"], [1, 19])
 
 
-def run_sampled_parity(cfg, heads, seed=0, n_steps=2, check_steps=(1,)):
+def run_sampled_parity(cfg, heads, seed=0, n_steps=2, check_steps=(1,), residual="f32"):
     """Full-size layers: the GPU runs every row; the oracle checks sampled query
     blocks (first, text/video boundary, middle, ragged last) of sampled heads."""
     sh = rettn.shape_of(cfg)
@@ -165,7 +176,7 @@ def run_sampled_parity(cfg, heads, seed=0, n_steps=2, check_steps=(1,)):
             qq, kk = gu.host(q0[b, h][None, None]), gu.host(k0[b, h][None, None])
             ref_idx[b, h] = oracle.select_blocks(qq, kk, N, d, keep, forced)[0, 0]
     idx = torch.as_tensor(ref_idx).to(gu.DEV)
-    cache = rettn.StatsCache(sh, 1)
+    cache = rettn.StatsCache(sh, 1, residual=residual)
     o_cal = gu.calibrate(sh, q0, k0, v0, idx, cache)
     torch.cuda.synchronize()
     t = cache.tensors(0)
@@ -198,6 +209,10 @@ def run_sampled_parity(cfg, heads, seed=0, n_steps=2, check_steps=(1,)):
                 ro = oracle.sparse_reshape_rows(qh, kh, vh, rows, ref_idx[b, h, i], st["m"], st["z_full"],
                                                 st["z_sparse"], st["r"], N, d)
                 gu.assert_close(gu.host(o[b, h, rows]), ro, what=f"step {s} O b{b} h{h} blk{i}")
+                if residual == "bf16":
+                    rs = oracle.sparse_reshape_rows(qh, kh, vh, rows, ref_idx[b, h, i], st["m"], st["z_full"],
+                                                    st["z_sparse"], bf16_round(st["r"]), N, d)
+                    gu.assert_close(gu.host(o[b, h, rows]), rs, what=f"step {s} O (rounded R) b{b} h{h} blk{i}")
     cache.close()
 
 
@@ -205,6 +220,39 @@ def test_parity_cogvideox2b_sampled():
     say("parity cogvideox2b sampled")
     cfg = configs.CONFIGS["cogvideox2b"]
     run_sampled_parity(cfg, heads=[(0, 0), (1, 29)], n_steps=4, check_steps=(1, 3))
+
+
+def test_parity_pixart1024_bf16_residual():
+    say("parity pixart1024 bf16 residual")
+    run_full_parity(configs.CONFIGS["pixart1024"], [1, 19], residual="bf16")
+
+
+def test_parity_cogvideox2b_sampled_bf16_residual():
+    say("parity cogvideox2b sampled bf16 residual")
+    cfg = configs.CONFIGS["cogvideox2b"]
+    run_sampled_parity(cfg, heads=[(0, 3), (1, 17)], n_steps=4, check_steps=(3,), residual="bf16")
+
+
+def test_bf16_residual_is_rounded_f32():
+    """A bf16-residual cache holds the float32 residual rounded to nearest even;
+    O, m, Z_full, Z_sparse and the list copy equal those of a float32 cache."""
+    say("bf16 residual = rounded f32 residual")
+    cfg = small_cfg("cogvideox2b", H=3)
+    sh = rettn.shape_of(cfg)
+    (q, k, v), = gu.gpu_inputs(cfg, 1, seed=11)
+    idx, _ = gu.select(sh, q, k, configs.forced_blocks(cfg))
+    c32, c16 = rettn.StatsCache(sh, 1), rettn.StatsCache(sh, 1, residual="bf16")
+    o32 = gu.calibrate(sh, q, k, v, idx, c32)
+    o16 = gu.calibrate(sh, q, k, v, idx, c16)
+    torch.cuda.synchronize()
+    t32, t16 = c32.tensors(0), c16.tensors(0)
+    assert t16["R"].dtype == torch.bfloat16 and t32["R"].dtype == torch.float32
+    assert torch.equal(o32, o16)
+    for name in ("m", "z_full", "z_sparse", "idx"):
+        assert torch.equal(t32[name], t16[name]), name
+    assert torch.equal(t16["R"], t32["R"].to(torch.bfloat16))
+    c32.close()
+    c16.close()
 
 
 # ------------------------------------------------------------------ identities on the GPU
