@@ -24,7 +24,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SRC = os.path.join(HERE, "csrc", "attn_bf16.hip")
 COPY_BYTES = 512 << 20
 
-SHORT = [("sparse_occ_kernel<64", "sparse reshape (d_pad 64)"), ("sparse_occ_kernel<80", "sparse reshape (d_pad 80)"),
+SHORT = [("sparse_occ_kernel<64, true>", "sparse reshape, bf16 residual (d_pad 64)"),
+         ("sparse_occ_kernel<80, true>", "sparse reshape, bf16 residual (d_pad 80)"),
+         ("sparse_occ_kernel<64", "sparse reshape (d_pad 64)"), ("sparse_occ_kernel<80", "sparse reshape (d_pad 80)"),
+         ("calib_kernel<64, 2, 2, true>", "calibration, bf16 residual (d_pad 64)"),
          ("calib_kernel<64", "calibration (d_pad 64)"), ("calib_kernel<80", "calibration (d_pad 80)"),
          ("attn_f32_kernel", "float32 attention"), ("select_kernel", "block top-k"), ("pool_kernel", "block pooling")]
 
