@@ -16,6 +16,8 @@ from .rettention import (  # noqa: F401
     sparse_reshape,
     calibrate_rows,
     sparse_reshape_rows,
+    sparse_reshape_r2,
+    sparse_reshape_rows_r2,
     closed_form_fp64,
     kept_flops,
 )

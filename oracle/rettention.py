@@ -29,6 +29,11 @@ b, head h, with alpha = 1/sqrt(d) for the true head dim d and 64-token blocks:
   sparse step s_j over kept keys only, m, Z = sum e^{s-m}, N = sum e^{s-m} v,
               M = max(m, m_c),
               O = (N e^{m-M} + R_c e^{m_c-M}) / (Z e^{m-M} Z_full_c / Z_sparse_c).
+  variant R2  (a second reading of the same paragraph, kept as an option: the
+              cached ratio r_c = Z_sparse_c / Z_full_c weights the step's
+              renormalised sparse output against the cached masked part)
+              O = r_c N / Z + R_c / Z_full_c
+                = r_c O_sparse + (1 - r_c) R_c / (Z_full_c - Z_sparse_c).
 
 Everything is computed in ``dtype`` (float64 unless asked otherwise) from the
 stored input values.
@@ -148,6 +153,37 @@ def sparse_reshape_rows(q, k, v, rows, idx_row, m_c, z_full_c, z_sparse_c, r_c, 
     num = n * np.exp(m - big)[:, None] + r_c * np.exp(m_c - big)[:, None]
     den = z * np.exp(m - big) * z_full_c / z_sparse_c
     return num / den[:, None]
+
+
+def sparse_reshape_rows_r2(q, k, v, rows, idx_row, z_full_c, z_sparse_c, r_c, N, d,
+                           block=BLOCK, dtype=np.float64):
+    """Reshape variant R2 for query rows ``rows`` of one head: the step's sparse
+    attention output over the kept keys (softmax renormalised over them),
+    weighted by the cached ratio, plus the cached masked part R_c / Z_full_c.
+    Both terms are free of any max shift (R_c and Z_full_c share one)."""
+    q, k, v = (_np(t, dtype) for t in (q, k, v))
+    z_full_c, z_sparse_c, r_c = (_np(t, dtype) for t in (z_full_c, z_sparse_c, r_c))
+    alpha = dtype(1.0) / np.sqrt(dtype(d))
+    kept = _kept_mask(idx_row, N, block)
+    K, V = k[:N][kept], v[:N][kept]
+    s = alpha * (q[rows] @ K.T)
+    p = np.exp(s - s.max(axis=1)[:, None])
+    o_sparse = (p @ V) / p.sum(axis=1)[:, None]
+    return (z_sparse_c / z_full_c)[:, None] * o_sparse + r_c / z_full_c[:, None]
+
+
+def sparse_reshape_r2(q, k, v, idx, cache, N, d, block=BLOCK, dtype=np.float64):
+    """Reshape variant R2 over a whole layer with the cached statistics ``cache``."""
+    q, k, v = (_np(t, dtype) for t in (q, k, v))
+    B, H, _, D = q.shape
+    o = np.zeros((B, H, N, D), dtype)
+    for b in range(B):
+        for h in range(H):
+            for i, (a, e) in enumerate(block_ranges(N, block)):
+                o[b, h, a:e] = sparse_reshape_rows_r2(
+                    q[b, h], k[b, h], v[b, h], slice(a, e), idx[b, h, i], cache["z_full"][b, h, a:e],
+                    cache["z_sparse"][b, h, a:e], cache["r"][b, h, a:e], N, d, block, dtype)
+    return o
 
 
 def calibrate(q, k, v, idx, N, d, block=BLOCK, dtype=np.float64):

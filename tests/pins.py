@@ -206,6 +206,61 @@ def pin_selector(orc):
     return float(bad)
 
 
+# ---------------------------------------------------------------- reshape variant R2
+def pin_r2_calibration_identity(orc):
+    """R2 on the calibration inputs gives dense attention (as R1 does)."""
+    q, k, v, _, _, _ = small_case()
+    N, d = 200, 24
+    idx = orc.select_blocks(q, k, N, d, keep=2, forced=[1])
+    st = orc.calibrate(q, k, v, idx, N, d)
+    return rel(orc.sparse_reshape_r2(q, k, v, idx, st, N, d), sdpa64(q, k, v, N, d))
+
+
+def pin_r2_keep_all(orc):
+    """R2 with every block kept gives dense attention at a later step."""
+    q0, k0, v0, q1, k1, v1 = small_case()
+    N, d = 200, 24
+    nb = (N + BLOCK - 1) // BLOCK
+    idx = orc.select_blocks(q0, k0, N, d, keep=nb)
+    st = orc.calibrate(q0, k0, v0, idx, N, d)
+    return rel(orc.sparse_reshape_r2(q1, k1, v1, idx, st, N, d), sdpa64(q1, k1, v1, N, d))
+
+
+def pin_r2_closed_form(orc):
+    """R2 = r O_sparse + (1 - r) O_masked with library pieces: masked attention of
+    the later step over the listed blocks, masked attention of the calibration
+    step over the other blocks, and r = exp(logsumexp_kept - logsumexp_all) of
+    the calibration logits."""
+    q0, k0, v0, q1, k1, v1 = small_case(N=190)
+    N, d = 190, 24
+    idx = orc.select_blocks(q0, k0, N, d, keep=2, forced=[0])
+    st = orc.calibrate(q0, k0, v0, idx, N, d)
+    mask = block_mask(idx, N)
+    o_sparse = sdpa64(q1, k1, v1, N, d, mask=mask)
+    o_masked = sdpa64(q0, k0, v0, N, d, mask=~mask)
+    s0 = torch.as_tensor(q0[..., :N, :]) @ torch.as_tensor(k0[..., :N, :]).transpose(-1, -2) / np.sqrt(d)
+    lse_all = torch.logsumexp(s0, dim=-1)
+    lse_kept = torch.logsumexp(s0.masked_fill(~torch.as_tensor(mask), float("-inf")), dim=-1)
+    r = torch.exp(lse_kept - lse_all).numpy()[..., None]
+    return rel(orc.sparse_reshape_r2(q1, k1, v1, idx, st, N, d), r * o_sparse + (1 - r) * o_masked)
+
+
+def pin_r2_logit_offset(orc):
+    """R2 ignores a uniform per-row logit offset at the sparse step: a padding
+    channel that adds delta_t to every logit of row t (q_t[c] = delta_t sqrt(d),
+    k_j[c] = 1) leaves the output unchanged."""
+    q0, k0, v0, q1, k1, v1 = small_case()
+    N, d, c = 200, 24, 30
+    idx = orc.select_blocks(q0, k0, N, d, keep=2)
+    st = orc.calibrate(q0, k0, v0, idx, N, d)
+    o = orc.sparse_reshape_r2(q1, k1, v1, idx, st, N, d)
+    delta = np.random.default_rng(7).uniform(-4.0, 6.0, size=q1.shape[:-1])
+    q1s, k1s = q1.copy(), k1.copy()
+    q1s[..., c] = delta * np.sqrt(d)
+    k1s[..., c] = 1.0
+    return rel(orc.sparse_reshape_r2(q1s, k1s, v1, idx, st, N, d), o)
+
+
 ALL_PINS = {
     "calibration_identity": (pin_calibration_identity, 1e-10),
     "keep_all": (pin_keep_all, 1e-10),
@@ -217,6 +272,10 @@ ALL_PINS = {
     "pooling": (pin_pooling, 1e-12),
     "pooled_scores": (pin_pooled_scores, 1e-12),
     "selector": (pin_selector, 0.0),
+    "r2_calibration_identity": (pin_r2_calibration_identity, 1e-10),
+    "r2_keep_all": (pin_r2_keep_all, 1e-10),
+    "r2_closed_form": (pin_r2_closed_form, 1e-10),
+    "r2_logit_offset": (pin_r2_logit_offset, 1e-10),
 }
 
 

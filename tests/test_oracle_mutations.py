@@ -30,6 +30,10 @@ MUTATIONS = {
     "current_max_scale_dropped": ("n * np.exp(m - big)[:, None]", "n"),
     "kept_block_off_by_one": ("mask[j * block: min((j + 1) * block, N)] = True",
                               "mask[(j + 1) * block: min((j + 2) * block, N)] = True"),
+    "r2_ratio_inverted": ("(z_sparse_c / z_full_c)[:, None] * o_sparse", "(z_full_c / z_sparse_c)[:, None] * o_sparse"),
+    "r2_residual_over_sparse_denominator": ("+ r_c / z_full_c[:, None]", "+ r_c / z_sparse_c[:, None]"),
+    "r2_sparse_output_unnormalised": ("o_sparse = (p @ V) / p.sum(axis=1)[:, None]", "o_sparse = p @ V"),
+    "r2_residual_dropped": ("* o_sparse + r_c / z_full_c[:, None]", "* o_sparse"),
 }
 
 
