@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--all-configs", action="store_true",
                    help="print the per-kernel breakdown of every configuration, one JSON line each "
                         "(not the headline line)")
+    p.add_argument("--fidelity", action="store_true",
+                   help="reshape fidelity study over the denoising schedule (one JSON line; not the headline)")
+    p.add_argument("--period", type=int, default=10, help="recalibration period of the --fidelity study")
     return p.parse_args()
 
 
@@ -173,6 +176,12 @@ def components(cfg, reps=20, flush_mb=512):
     t_cal, _ = timed(cal, max(3, reps // 4))
     t_warm, pw = timed(spa, reps)
     t_cold, pc = timed(spa, reps, cold=True)
+    # reshape variant R2 (r * normalised sparse output + R / Z_full) on the same cache
+    spa2 = lambda: rettn.rt_sparse_attn_reshape_ex(sh, q1, k1, v1, None, cache, 0, "r2", out)
+    spa2()
+    torch.cuda.synchronize()
+    t2w, _ = timed(spa2, reps)
+    t2c, _ = timed(spa2, reps, cold=True)
     # the same with the residual cached in bf16 (cache option; float32 is the baseline)
     t16w = t16c = None
     if cfg["dtype"] == "bf16":
@@ -204,9 +213,90 @@ def components(cfg, reps=20, flush_mb=512):
         "sparse_bf16_residual_warm_ms": None if t16w is None else round(t16w, 5),
         "sparse_bf16_residual_cold_ms": None if t16c is None else round(t16c, 5),
         "sparse_bf16_residual_alg_bytes": None if t16w is None else byts - sh.B * sh.H * N * D * 2,
+        "sparse_r2_warm_ms": round(t2w, 5), "sparse_r2_cold_ms": round(t2c, 5),
+        "sparse_r2_alg_bytes": byts - sh.B * sh.H * N * 4,  # no cached row max
     }
     cache.close()
     return res
+
+
+def fidelity(cfg, period):
+    """How close each sparse step is to dense attention over a denoising
+    schedule, on the GPU path alone.  Dense attention of every step comes from
+    rt_calibrate (its output is dense attention; a second cache is recalibrated
+    each step with the step-0 lists, which also gives r_t = Z_sparse/Z_full of
+    that step for the fixed mask).  Compared per step, as L1 error relative to
+    the dense output's L1 norm:
+      * plain sparse attention over the step-0 lists (no reshape: a copy of the
+        step-0 cache with Z_sparse = Z_full and R = 0 makes both epilogues
+        compute exactly that);
+      * R1 and R2 from the step-0 cache (one calibration, lists fixed);
+      * R1 and R2 with recalibration (fresh lists) every `period` steps.
+    Also per step: the median and 90th percentile over rows of |r_t/r_0 - 1|
+    and of |m_t - m_0| (cached row max, logit units) for the fixed mask."""
+    import numpy as np
+    import torch
+    from sparse_attention_diffusion_amd import configs, rettn, synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sh = rettn.shape_of(cfg)
+    N, D, keep = cfg["N"], cfg["d_pad"], cfg["keep"]
+    forced = configs.forced_blocks(cfg)
+    nb = configs.n_blocks(N)
+    it = synth.StepInputs(cfg, seed=0, device=dev)
+    c0, cdense, cplain, cper = (rettn.StatsCache(sh, 1, device=dev) for _ in range(4))
+    idx = torch.empty((sh.B, sh.H, nb, keep), dtype=torch.int32, device=dev)
+    ws = torch.empty(rettn.select_workspace_bytes(sh), dtype=torch.uint8, device=dev)
+    new = lambda: torch.empty((sh.B, sh.H, N, D), dtype=rettn.torch_dtype(sh), device=dev)
+    o_dense, o = new(), new()
+
+    def err(a, ref):
+        a, ref = a.float(), ref.float()
+        return float((a - ref).abs().sum() / ref.abs().sum())
+
+    q, k, v = (synth.store(x, cfg["dtype"]) for x in it.next())
+    rettn.rt_select_blocks(sh, q, k, forced, idx, None, ws)
+    rettn.rt_calibrate(sh, q, k, v, idx, c0, 0, o_dense)
+    rettn.rt_calibrate(sh, q, k, v, idx, cper, 0, o_dense)
+    t0, tp = c0.tensors(0), cplain.tensors(0)
+    for name in ("m", "z_full", "idx"):
+        tp[name].copy_(t0[name])
+    tp["z_sparse"].copy_(t0["z_full"])
+    tp["R"].zero_()
+    cplain.set_valid(0)
+    r0 = (t0["z_sparse"] / t0["z_full"]).clone()
+    m0 = t0["m"].clone()
+    rows = []
+    for s in range(1, cfg["steps"]):
+        q, k, v = (synth.store(x, cfg["dtype"]) for x in it.next())
+        rettn.rt_calibrate(sh, q, k, v, idx, cdense, 0, o_dense)
+        td = cdense.tensors(0)
+        dr = ((td["z_sparse"] / td["z_full"]) / r0 - 1).abs().flatten()
+        dm = (td["m"] - m0).abs().flatten()
+        pick = torch.randperm(dr.numel(), device=dev)[: 1 << 20]
+        qr = torch.quantile(dr[pick], torch.tensor([0.5, 0.9], device=dev)).tolist()
+        qm = torch.quantile(dm[pick], torch.tensor([0.5, 0.9], device=dev)).tolist()
+        rec = {"step": s, "r_drift_p50": qr[0], "r_drift_p90": qr[1], "m_drift_p50": qm[0], "m_drift_p90": qm[1]}
+        rettn.rt_sparse_attn_reshape_ex(sh, q, k, v, None, cplain, 0, "r2", o)
+        rec["plain"] = err(o, o_dense)
+        for var in ("r1", "r2"):
+            rettn.rt_sparse_attn_reshape_ex(sh, q, k, v, None, c0, 0, var, o)
+            rec[var] = err(o, o_dense)
+        if s % period == 0:
+            rettn.rt_select_blocks(sh, q, k, forced, idx, None, ws)  # fresh lists for this cache only
+            rettn.rt_calibrate(sh, q, k, v, idx, cper, 0, o)
+            rec["r1_period"] = rec["r2_period"] = err(o, o_dense)
+            idx.copy_(t0["idx"])
+        else:
+            for var in ("r1", "r2"):
+                rettn.rt_sparse_attn_reshape_ex(sh, q, k, v, None, cper, 0, var, o)
+                rec[var + "_period"] = err(o, o_dense)
+        rows.append({k_: (round(v_, 6) if isinstance(v_, float) else v_) for k_, v_ in rec.items()})
+    for c in (c0, cdense, cplain, cper):
+        c.close()
+    return {"study": "reshape fidelity vs dense attention", "config": cfg.get("name"), "period": period,
+            "data": "synthetic drift inputs, seed 0", "metric": "L1(O - O_dense) / L1(O_dense) per step",
+            "steps": rows}
 
 
 def _cpu_model():
@@ -229,6 +319,9 @@ def main():
     import torch
     from sparse_attention_diffusion_amd import configs, rettn, synth
 
+    if args.fidelity:
+        print(json.dumps(fidelity(dict(configs.CONFIGS[args.config], name=args.config), args.period)), flush=True)
+        return
     if args.all_configs:
         torch.cuda.set_device(0)
         for name in configs.CONFIGS:
@@ -325,7 +418,7 @@ def main():
                  "frac": round(tflops / PEAK_BF16_TFLOPS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": "rt_sparse_attn_reshape (sparse_occ_kernel<64>)",
+                     "kernel": "rt_sparse_attn_reshape (sparse_occ_kernel<64, false, false>)",
                      "algorithmic_bytes_per_launch": byts},
         "pages_context": {"kept_fraction": round(keep / configs.n_blocks(N), 4),
                           "skipped_fraction": round(1 - flop / (4 * d * N * N * cfg["B"] * cfg["H"]), 4)},

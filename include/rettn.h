@@ -171,6 +171,25 @@ rt_status rt_sparse_attn_reshape(const rt_shape* shape, const void* q, const voi
                                  const rt_stats_cache* cache, int32_t layer, void* o,
                                  void* stream);
 
+/* ---- sparse step, choice of reshape (core-mechanism paragraph) ----
+ * The page fixes the reshape on the calibration step (sparse denominator
+ * scaled by the cached full/sparse ratio, cached masked residual added) but
+ * leaves open how the residual is weighted at a later step; two readings:
+ *   RT_RESHAPE_R1 (what rt_sparse_attn_reshape computes): the residual keeps
+ *     its calibration-step magnitude relative to the current running max,
+ *     O = (N e^{m-M} + R_c e^{m_c-M}) / (Z e^{m-M} Zf_c / Zs_c);
+ *   RT_RESHAPE_R2: the calibration step's split of attention mass is reused,
+ *     O = r_c N / Z + R_c / Zf_c with r_c = Zs_c / Zf_c; it is independent of
+ *     the cached row max and of any uniform logit offset at the later step.
+ * Both equal dense attention on the calibration step's own inputs.  Any other
+ * `variant` is RT_E_ARG; otherwise arguments and errors as for
+ * rt_sparse_attn_reshape.                                                   */
+enum { RT_RESHAPE_R1 = 0, RT_RESHAPE_R2 = 1 };
+rt_status rt_sparse_attn_reshape_ex(const rt_shape* shape, const void* q, const void* k,
+                                    const void* v, const int32_t* block_idx,
+                                    const rt_stats_cache* cache, int32_t layer, int32_t variant,
+                                    void* o, void* stream);
+
 /* ---- denoising schedule (teaser paragraph: statistics reused across steps) ----
  * 1 if `step` is a calibration step for `period` (period <= 0: only step 0).   */
 int32_t rt_schedule_is_calibration(int32_t step, int32_t period);

@@ -347,6 +347,14 @@ rt_status rt_calibrate(const rt_shape* s, const void* q, const void* k, const vo
 rt_status rt_sparse_attn_reshape(const rt_shape* s, const void* q, const void* k, const void* v,
                                  const int32_t* block_idx, const rt_stats_cache* c, int32_t layer, void* o,
                                  void* stream) {
+  return rt_sparse_attn_reshape_ex(s, q, k, v, block_idx, c, layer, RT_RESHAPE_R1, o, stream);
+}
+
+rt_status rt_sparse_attn_reshape_ex(const rt_shape* s, const void* q, const void* k, const void* v,
+                                    const int32_t* block_idx, const rt_stats_cache* c, int32_t layer,
+                                    int32_t variant, void* o, void* stream) {
+  if (variant != RT_RESHAPE_R1 && variant != RT_RESHAPE_R2)
+    return fail(RT_E_ARG, "reshape variant must be RT_RESHAPE_R1 or RT_RESHAPE_R2 (got %d)", variant);
   rt_status st = check_shape(s);
   if (st != RT_OK) return st;
   if ((st = check_cache(s, c, layer)) != RT_OK) return st;
@@ -360,6 +368,7 @@ rt_status rt_sparse_attn_reshape(const rt_shape* s, const void* q, const void* k
   AttnArgs a = attn_args(s, q, k, v, o, nullptr, c, layer);
   a.idx = block_idx != nullptr ? block_idx : a.idx_cache;
   a.idx_cache = nullptr;
+  a.variant = variant;
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e = s->dtype == RT_BF16 ? rettn::launch_attn_bf16(AttnMode::kSparse, s->d_pad, a, hs)
                                      : rettn::launch_attn_f32(AttnMode::kSparse, s->d_pad, a, hs);

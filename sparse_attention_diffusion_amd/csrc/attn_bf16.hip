@@ -478,29 +478,39 @@ struct PipeItem {
   __device__ __forceinline__ int block(int n, int Nb) const { return min(max(list[n], 0), Nb - 1); }
 };
 
-// One query block's per-lane data, loaded a block ahead: Q^T operand,
-// statistics and residual (in accumulator order).  KS + 3 + D/8 loads.
+// One query block's per-lane statistics (the cached row max only for the
+// R1 epilogue, which needs the residual's reference).
 template <int D>
 struct PipeStats {
   float mc, zf, zs;
 };
 
-template <int D, bool RB>
-__device__ __forceinline__ void pipe_load(bf16x8 (&q)[Shape<D>::KS], PipeStats<D>& st, f32x4 (&r)[Shape<D>::NT][4],
-                                          const AttnArgs& a, int bh, int qi, int rowq, int g) {
+// Q^T operand and statistics of one query block: KS + 3 loads (KS + 2 for R2).
+template <int D, bool R2>
+__device__ __forceinline__ void load_qs(bf16x8 (&q)[Shape<D>::KS], PipeStats<D>& st, const AttnArgs& a, int bh,
+                                        int qi, int rowq, int g) {
   const size_t r0 = (size_t)bh * a.N + (size_t)qi * kBlock;  // first row of the block
   const int rows = min(a.N - qi * kBlock, kBlock);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)a.q + r0 * D * 2, rows * D * 2);
-  const __amdgpu_buffer_rsrc_t rr =
-      RB ? make_rsrc((const __bf16*)a.R + r0 * D, rows * D * 2) : make_rsrc(a.R + r0 * D, rows * D * 4);
 #pragma unroll
   for (int ks = 0; ks < Shape<D>::KS; ++ks)
     q[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, (rowq * D + 16 * ks + 8 * g) * 2, 0, 0));
-  st.mc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.m + r0, rows * 4), rowq * 4, 0, 0));
+  if (!R2)
+    st.mc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.m + r0, rows * 4), rowq * 4, 0, 0));
   st.zf = __builtin_bit_cast(float,
                              __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.z_full + r0, rows * 4), rowq * 4, 0, 0));
   st.zs = __builtin_bit_cast(float,
                              __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.z_sparse + r0, rows * 4), rowq * 4, 0, 0));
+}
+
+// Cached residual of one query block in accumulator order: D/8 loads.
+template <int D, bool RB>
+__device__ __forceinline__ void load_residual(f32x4 (&r)[Shape<D>::NT][4], const AttnArgs& a, int bh, int qi, int rowq,
+                                              int g) {
+  const size_t r0 = (size_t)bh * a.N + (size_t)qi * kBlock;
+  const int rows = min(a.N - qi * kBlock, kBlock);
+  const __amdgpu_buffer_rsrc_t rr =
+      RB ? make_rsrc((const __bf16*)a.R + r0 * D, rows * D * 2) : make_rsrc(a.R + r0 * D, rows * D * 4);
 #pragma unroll
   for (int t = 0; t < Shape<D>::NT; ++t)
 #pragma unroll
@@ -556,15 +566,19 @@ __device__ __forceinline__ void probs_ref(bf16x8 (&p)[2][2], const f32x16 (&s)[2
 // A query block's accumulator starts as its cached residual R with the
 // reference max at the cached m (R is stored relative to m); the lazy max
 // update rescales both parts together, so the reshape epilogue is
-// O = acc * Z_sparse / (Z * Z_full) with Z the kept mass.  All global traffic
-// goes through buffer resources whose byte limit zero-fills rows past N on
-// loads and drops them on stores.
-template <int D, bool RB>
+// O = acc * Z_sparse / (Z * Z_full) with Z the kept mass.
+// Variant R2 (V2) instead blends the normalised sparse output with the cached
+// masked output: the accumulator starts at zero with no reference max, the
+// residual is fetched in the epilogue, which computes
+// O = acc * Z_sparse / (Z * Z_full) + R / Z_full.  All global traffic goes
+// through buffer resources whose byte limit zero-fills rows past N on loads
+// and drops them on stores.
+template <int D, bool RB, bool V2>
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 3, 4)))
 sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
   constexpr int NT = Shape<D>::NT, KS = Shape<D>::KS, TILE = Shape<D>::TILE, ROW = Shape<D>::ROW;
   constexpr int NST = D / 8;          // O stores (and residual loads) per lane
-  constexpr int NLD = KS + NST + 3;   // per-query-block loads (Q, residual, statistics)
+  constexpr int NLD = V2 ? KS + 2 : KS + NST + 3;  // per-query-block loads (Q, statistics, R1: residual)
   __shared__ __attribute__((aligned(1024))) char ring[2 * TILE];  // K slot, V slot
   char* const kslot = ring;
   char* const vslot = ring + TILE;
@@ -621,20 +635,26 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
   bf16x8 q[KS];
   f32x16 o[NT];
   PipeStats<D> st;
-  // Q, statistics and residual (straight into the accumulator) of query block
-  // `it`: NLD loads.
+  // Q, statistics and (R1) the residual, straight into the accumulator, of
+  // query block `it`: NLD loads.
   auto load_rows = [&]() {
-    f32x4 r[NT][4];
-    pipe_load<D, RB>(q, st, r, a, it.bh, it.qi, rowq, g);
+    load_qs<D, V2>(q, st, a, it.bh, it.qi, rowq, g);
+    if (V2) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NT; ++t) o[t] = f32x16{};
+    } else {
+      f32x4 r[NT][4];
+      load_residual<D, RB>(r, a, it.bh, it.qi, rowq, g);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[t][i] = r[t][i >> 2][i & 3];
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[t][i] = r[t][i >> 2][i & 3];
+    }
   };
   load_rows();
 
   for (int k = 0; k < n_items; ++k) {
-    float mr = st.mc * kLog2e, z = 0.f;
+    float mr = V2 ? -INFINITY : st.mc * kLog2e, z = 0.f;
     for (int n = 0; n < keep; ++n) {
       // 1. K_n has landed (the loads issued after it may still be in flight).
       if (n == 0 && k > 0) wait_vmcnt<NST + NLD>();
@@ -700,9 +720,16 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
           }
       }
     }
-    // O = acc * Z_sparse / (Z * Z_full); rows past N are dropped by the limit.
+    // O = acc * Z_sparse / (Z * Z_full) (+ R / Z_full for R2); rows past N
+    // are dropped by the limit.
     {
       const float w = st.zs / (pair_sum(z) * st.zf);
+      const float u = 1.f / st.zf;
+      f32x4 rv[NT][4];  // R2: the residual, fetched now (no registers are free during the tiles)
+      if (V2) {
+        load_residual<D, RB>(rv, a, it.bh, it.qi, rowq, g);
+        wait_vmcnt<0>();
+      }
       const size_t r0 = (size_t)it.bh * N + (size_t)it.qi * kBlock;
       const __amdgpu_buffer_rsrc_t ro = make_rsrc((const char*)a.o + r0 * D * 2, min(N - it.qi * kBlock, kBlock) * D * 2);
 #pragma unroll
@@ -712,7 +739,8 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
           if (32 * t + 8 * i4 < D) {
             __bf16 ob[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ob[e] = (__bf16)(o[t][4 * i4 + e] * w);
+            for (int e = 0; e < 4; ++e)
+              ob[e] = V2 ? (__bf16)fmaf(o[t][4 * i4 + e], w, rv[t][i4][e] * u) : (__bf16)(o[t][4 * i4 + e] * w);
             __builtin_amdgcn_raw_buffer_store_b64(*(u32x2*)ob, ro, (rowq * D + 32 * t + 8 * i4 + 4 * g) * 2, 0, 0);
           }
     }
@@ -724,12 +752,16 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
   }
 }
 
-// Both residual types of the sparse kernel, instantiated explicitly (the host
-// compiler otherwise emits the launch stub of only one of them).
-template __global__ void sparse_occ_kernel<64, false>(AttnArgs, PersistGrid);
-template __global__ void sparse_occ_kernel<64, true>(AttnArgs, PersistGrid);
-template __global__ void sparse_occ_kernel<80, false>(AttnArgs, PersistGrid);
-template __global__ void sparse_occ_kernel<80, true>(AttnArgs, PersistGrid);
+// Every residual type and epilogue of the sparse kernel, instantiated
+// explicitly (the host compiler otherwise emits the launch stub of only one).
+template __global__ void sparse_occ_kernel<64, false, false>(AttnArgs, PersistGrid);
+template __global__ void sparse_occ_kernel<64, true, false>(AttnArgs, PersistGrid);
+template __global__ void sparse_occ_kernel<80, false, false>(AttnArgs, PersistGrid);
+template __global__ void sparse_occ_kernel<80, true, false>(AttnArgs, PersistGrid);
+template __global__ void sparse_occ_kernel<64, false, true>(AttnArgs, PersistGrid);
+template __global__ void sparse_occ_kernel<64, true, true>(AttnArgs, PersistGrid);
+template __global__ void sparse_occ_kernel<80, false, true>(AttnArgs, PersistGrid);
+template __global__ void sparse_occ_kernel<80, true, true>(AttnArgs, PersistGrid);
 
 // ---------------------------------------------------------------- calibration step
 template <int D, int NBUF, int QB>
@@ -896,10 +928,17 @@ hipError_t launch_d(AttnMode mode, const AttnArgs& a, hipStream_t s) {
     const uint32_t total = (uint32_t)a.BH * (uint32_t)a.Nb;
     PersistGrid pg{total, (total + 7u) / 8u, 0u};
     pg.g = min(pg.per, (uint32_t)(D == 64 ? kSparseWgPerXcd64 : kSparseWgPerXcd80));
-    if (a.r_bf16) {
-      hipLaunchKernelGGL((sparse_occ_kernel<D, true>), dim3(8u * pg.g), dim3(128), 0, s, a, pg);
+    const dim3 grid(8u * pg.g), block(128);
+    if (a.variant == 1) {
+      if (a.r_bf16)
+        hipLaunchKernelGGL((sparse_occ_kernel<D, true, true>), grid, block, 0, s, a, pg);
+      else
+        hipLaunchKernelGGL((sparse_occ_kernel<D, false, true>), grid, block, 0, s, a, pg);
     } else {
-      hipLaunchKernelGGL((sparse_occ_kernel<D, false>), dim3(8u * pg.g), dim3(128), 0, s, a, pg);
+      if (a.r_bf16)
+        hipLaunchKernelGGL((sparse_occ_kernel<D, true, false>), grid, block, 0, s, a, pg);
+      else
+        hipLaunchKernelGGL((sparse_occ_kernel<D, false, false>), grid, block, 0, s, a, pg);
     }
   } else {
     constexpr int QB = 2;  // 2*QB waves must divide the LDS row units; 2 workgroups per CU

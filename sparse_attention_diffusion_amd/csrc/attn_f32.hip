@@ -127,6 +127,12 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnArgs a, XcdGrid 
       rrow[d] = o[d];
       orow[d] = (ok[d] * corr + o[d]) / zf;
     }
+  } else if (a.variant == 1) {  // R2: r * O_sparse + R / Z_full
+    const float zf_c = a.z_full[srow], zs_c = a.z_sparse[srow];
+    const float w = zs_c / (zf_c * z);
+    const float* rrow = a.R + srow * D;
+#pragma unroll
+    for (int d = 0; d < D; ++d) orow[d] = fmaf(o[d], w, rrow[d] / zf_c);
   } else {
     const float m_c = a.m[srow], zf_c = a.z_full[srow], zs_c = a.z_sparse[srow];
     const float big = fmaxf(m, m_c);

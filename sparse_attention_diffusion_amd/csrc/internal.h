@@ -25,6 +25,8 @@ struct AttnArgs {
   int32_t BH, N, Nb, keep;
   float alpha;             // 1/sqrt(d)
   int32_t r_bf16;          // residual stored as bf16 (bf16 kernels only)
+  int32_t variant;         // sparse epilogue: 0 = R1 (residual rescaled by exp(m_c - M)),
+                           // 1 = R2 (r * normalised sparse output + R / Z_full)
 };
 
 struct SelectArgs {

@@ -24,9 +24,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SRC = os.path.join(HERE, "csrc", "attn_bf16.hip")
 COPY_BYTES = 512 << 20
 
-SHORT = [("sparse_occ_kernel<64, true>", "sparse reshape, bf16 residual (d_pad 64)"),
-         ("sparse_occ_kernel<80, true>", "sparse reshape, bf16 residual (d_pad 80)"),
-         ("sparse_occ_kernel<64", "sparse reshape (d_pad 64)"), ("sparse_occ_kernel<80", "sparse reshape (d_pad 80)"),
+SHORT = [("sparse_occ_kernel<64, false, false>", "sparse reshape R1 (d_pad 64)"),
+         ("sparse_occ_kernel<64, true, false>", "sparse reshape R1, bf16 residual (d_pad 64)"),
+         ("sparse_occ_kernel<64, false, true>", "sparse reshape R2 (d_pad 64)"),
+         ("sparse_occ_kernel<64, true, true>", "sparse reshape R2, bf16 residual (d_pad 64)"),
+         ("sparse_occ_kernel<80, false, false>", "sparse reshape R1 (d_pad 80)"),
+         ("sparse_occ_kernel<80, true, false>", "sparse reshape R1, bf16 residual (d_pad 80)"),
+         ("sparse_occ_kernel<80, false, true>", "sparse reshape R2 (d_pad 80)"),
+         ("sparse_occ_kernel<80, true, true>", "sparse reshape R2, bf16 residual (d_pad 80)"),
          ("calib_kernel<64, 2, 2, true>", "calibration, bf16 residual (d_pad 64)"),
          ("calib_kernel<64", "calibration (d_pad 64)"), ("calib_kernel<80", "calibration (d_pad 80)"),
          ("attn_f32_kernel", "float32 attention"), ("select_kernel", "block top-k"), ("pool_kernel", "block pooling")]
@@ -108,7 +113,7 @@ def main():
         for k in sorted(set(fetch) | set(write)):
             f, w = fetch.get(k, 0.0), write.get(k, 0.0)
             lines.append(f"| {k} | {f / 1e6:.1f} | {w / 1e6:.1f} | {(f + w) / 1e6:.1f} |")
-        label = "sparse reshape (d_pad 64)"
+        label = "sparse reshape R1 (d_pad 64)"
         if label in fetch and label in write:
             rec = dict(config=args.config, kernel=label, kernel_source_sha256_16=source_hash(),
                        fetch_bytes=fetch[label], write_bytes=write[label],

@@ -56,6 +56,7 @@ def _load():
         "rt_stats_cache_destroy": (I32, [P]),
         "rt_calibrate": (I32, [S, P, P, P, P, P, I32, P, P]),
         "rt_sparse_attn_reshape": (I32, [S, P, P, P, P, P, I32, P, P]),
+        "rt_sparse_attn_reshape_ex": (I32, [S, P, P, P, P, P, I32, I32, P, P]),
         "rt_schedule_is_calibration": (I32, [I32, I32]),
         "rt_step_workspace_bytes": (SZ, [S]),
         "rt_attention_step": (I32, [S, P, P, P, ctypes.POINTER(I32), I32, P, I32, I32, I32, P, P, SZ, P,
@@ -74,7 +75,7 @@ SYMBOLS = [
     "rt_select_blocks", "rt_stats_cache_bytes", "rt_stats_cache_init", "rt_stats_cache_bytes_ex",
     "rt_stats_cache_init_ex", "rt_stats_cache_view",
     "rt_stats_cache_set_valid", "rt_stats_cache_invalidate", "rt_stats_cache_destroy", "rt_calibrate",
-    "rt_sparse_attn_reshape", "rt_schedule_is_calibration", "rt_step_workspace_bytes", "rt_attention_step",
+    "rt_sparse_attn_reshape", "rt_sparse_attn_reshape_ex", "rt_schedule_is_calibration", "rt_step_workspace_bytes", "rt_attention_step",
 ]
 
 
@@ -220,6 +221,19 @@ def rt_calibrate(sh, q, k, v, block_idx, cache, layer, o, stream=None):
 def rt_sparse_attn_reshape(sh, q, k, v, block_idx, cache, layer, o, stream=None):
     _check(_lib.rt_sparse_attn_reshape(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx),
                                        cache.handle, layer, _ptr(o), _stream(stream)))
+
+
+RT_RESHAPE_R1, RT_RESHAPE_R2 = 0, 1
+_VARIANTS = {"r1": RT_RESHAPE_R1, "r2": RT_RESHAPE_R2}
+
+
+def rt_sparse_attn_reshape_ex(sh, q, k, v, block_idx, cache, layer, variant, o, stream=None):
+    """`variant`: "r1" / "r2" or the RT_RESHAPE_* value."""
+    var = _VARIANTS.get(variant, variant) if isinstance(variant, str) else int(variant)
+    if isinstance(var, str):
+        raise ValueError(f"unknown reshape variant {variant!r}")
+    _check(_lib.rt_sparse_attn_reshape_ex(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx),
+                                          cache.handle, layer, var, _ptr(o), _stream(stream)))
 
 
 def rt_attention_step(sh, q, k, v, forced, cache, layer, step, period, o, workspace, stream=None):

@@ -78,9 +78,14 @@ def calibrate(sh, q, k, v, idx, cache, layer=0):
     return o
 
 
-def sparse(sh, q, k, v, cache, layer=0, idx=None):
+def sparse(sh, q, k, v, cache, layer=0, idx=None, variant=None):
+    """Sparse step through rt_sparse_attn_reshape, or through the _ex entry
+    point when a reshape variant ("r1" / "r2") is named."""
     o = empty_out(sh)
-    rettn.rt_sparse_attn_reshape(sh, q, k, v, idx, cache, layer, o)
+    if variant is None:
+        rettn.rt_sparse_attn_reshape(sh, q, k, v, idx, cache, layer, o)
+    else:
+        rettn.rt_sparse_attn_reshape_ex(sh, q, k, v, idx, cache, layer, variant, o)
     return o
 
 

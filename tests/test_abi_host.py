@@ -194,6 +194,11 @@ def test_state_machine_without_gpu():
     p = ctypes.c_void_p(4096)
     assert lib.rt_sparse_attn_reshape(ctypes.byref(sh), p, p, p, None, h, 0, p, None) == rettn.RT_E_STATE
     assert lib.rt_sparse_attn_reshape(ctypes.byref(sh), p, p, p, None, h, 2, p, None) == rettn.RT_E_ARG
+    for var in (rettn.RT_RESHAPE_R1, rettn.RT_RESHAPE_R2):
+        assert lib.rt_sparse_attn_reshape_ex(ctypes.byref(sh), p, p, p, None, h, 0, var, p, None) == rettn.RT_E_STATE
+    for bad in (-1, 2, 7):  # the variant is checked first
+        assert lib.rt_sparse_attn_reshape_ex(ctypes.byref(sh), p, p, p, None, h, 0, bad, p, None) == rettn.RT_E_ARG
+        assert b"variant" in lib.rt_last_error()
     other = rettn.shape(1, 1, 128, 64, 64, 2)
     assert lib.rt_calibrate(ctypes.byref(other), p, p, p, p, h, 0, p, None) == rettn.RT_E_STATE
     assert lib.rt_calibrate(ctypes.byref(sh), p, p, p, None, h, 0, p, None) == rettn.RT_E_ARG

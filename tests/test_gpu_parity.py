@@ -100,7 +100,18 @@ def bf16_round(x):
     return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).double().numpy()
 
 
-def run_full_parity(cfg, steps_to_check, seed=0, residual="f32"):
+def oracle_rows(variant, qh, kh, vh, rows, idx_row, st, r, N, d):
+    """The oracle's reshape of one query block for variant "r1" or "r2"."""
+    if variant == "r2":
+        return oracle.sparse_reshape_rows_r2(qh, kh, vh, rows, idx_row, st["z_full"], st["z_sparse"], r, N, d)
+    return oracle.sparse_reshape_rows(qh, kh, vh, rows, idx_row, st["m"], st["z_full"], st["z_sparse"], r, N, d)
+
+
+def oracle_layer(variant):
+    return oracle.sparse_reshape_r2 if variant == "r2" else oracle.sparse_reshape
+
+
+def run_full_parity(cfg, steps_to_check, seed=0, residual="f32", variant=None):
     """Oracle lists fed to the GPU; calibrate at step 0, reshape at later steps;
     the full layer is compared.  With a bf16 residual cache the later steps are
     checked against the oracle fed its residual rounded to bf16 and against the
@@ -130,12 +141,12 @@ def run_full_parity(cfg, steps_to_check, seed=0, residual="f32"):
     assert r_l1 <= 3e-3, r_l1
     for s in steps_to_check:
         q, k, v = stepsin[s]
-        o = gu.sparse(sh, q, k, v, cache)
+        o = gu.sparse(sh, q, k, v, cache, variant=variant)
         torch.cuda.synchronize()
-        ref_o = oracle.sparse_reshape(gu.host(q), gu.host(k), gu.host(v), ref_idx, ref_cal, N, d)
+        ref_o = oracle_layer(variant)(gu.host(q), gu.host(k), gu.host(v), ref_idx, ref_cal, N, d)
         res[f"step{s}"] = gu.assert_close(gu.host(o), ref_o, what=f"step {s} O", **tol)
         if residual == "bf16":
-            ref_s = oracle.sparse_reshape(gu.host(q), gu.host(k), gu.host(v), ref_idx, ref_cal_stored, N, d)
+            ref_s = oracle_layer(variant)(gu.host(q), gu.host(k), gu.host(v), ref_idx, ref_cal_stored, N, d)
             res[f"step{s}_stored"] = gu.assert_close(gu.host(o), ref_s, what=f"step {s} O (rounded R)", **tol)
     cache.close()
     return res
@@ -156,7 +167,7 @@ def test_parity_pixart1024():
     run_full_parity(configs.CONFIGS["pixart1024"], [1, 19])
 
 
-def run_sampled_parity(cfg, heads, seed=0, n_steps=2, check_steps=(1,), residual="f32"):
+def run_sampled_parity(cfg, heads, seed=0, n_steps=2, check_steps=(1,), residual="f32", variant=None):
     """Full-size layers: the GPU runs every row; the oracle checks sampled query
     blocks (first, text/video boundary, middle, ragged last) of sampled heads."""
     sh = rettn.shape_of(cfg)
@@ -199,19 +210,17 @@ def run_sampled_parity(cfg, heads, seed=0, n_steps=2, check_steps=(1,), residual
         q, k, v = (synth.store(x, cfg["dtype"]) for x in it.next())
         if s not in check_steps:
             continue
-        o = gu.sparse(sh, q, k, v, cache)
+        o = gu.sparse(sh, q, k, v, cache, variant=variant)
         torch.cuda.synchronize()
         for (b, h) in heads:
             qh, kh, vh = (gu.host(x[b, h]) for x in (q, k, v))
             for i in blocks:
                 rows = gu.block_rows(N, i)
                 st = refs[b, h, i]
-                ro = oracle.sparse_reshape_rows(qh, kh, vh, rows, ref_idx[b, h, i], st["m"], st["z_full"],
-                                                st["z_sparse"], st["r"], N, d)
+                ro = oracle_rows(variant, qh, kh, vh, rows, ref_idx[b, h, i], st, st["r"], N, d)
                 gu.assert_close(gu.host(o[b, h, rows]), ro, what=f"step {s} O b{b} h{h} blk{i}")
                 if residual == "bf16":
-                    rs = oracle.sparse_reshape_rows(qh, kh, vh, rows, ref_idx[b, h, i], st["m"], st["z_full"],
-                                                    st["z_sparse"], bf16_round(st["r"]), N, d)
+                    rs = oracle_rows(variant, qh, kh, vh, rows, ref_idx[b, h, i], st, bf16_round(st["r"]), N, d)
                     gu.assert_close(gu.host(o[b, h, rows]), rs, what=f"step {s} O (rounded R) b{b} h{h} blk{i}")
     cache.close()
 
@@ -231,6 +240,48 @@ def test_parity_cogvideox2b_sampled_bf16_residual():
     say("parity cogvideox2b sampled bf16 residual")
     cfg = configs.CONFIGS["cogvideox2b"]
     run_sampled_parity(cfg, heads=[(0, 3), (1, 17)], n_steps=4, check_steps=(3,), residual="bf16")
+
+
+# ------------------------------------------------------------------ reshape variant R2
+def test_parity_tiny_f32_r2():
+    say("parity tiny f32 r2")
+    run_full_parity(configs.CONFIGS["tiny"], [1], variant="r2")
+
+
+def test_parity_pixart1024_r2():
+    say("parity pixart1024 r2")
+    run_full_parity(configs.CONFIGS["pixart1024"], [1, 19], variant="r2")
+
+
+def test_parity_pixart512_r2_bf16_residual():
+    say("parity pixart512 r2 bf16 residual")
+    run_full_parity(configs.CONFIGS["pixart512"], [1, 9], residual="bf16", variant="r2")
+
+
+def test_parity_cogvideox2b_sampled_r2():
+    say("parity cogvideox2b sampled r2")
+    cfg = configs.CONFIGS["cogvideox2b"]
+    run_sampled_parity(cfg, heads=[(0, 7), (1, 23)], n_steps=4, check_steps=(1, 3), variant="r2")
+
+
+def test_r1_through_ex_is_the_default_entry_point():
+    """rt_sparse_attn_reshape_ex with RT_RESHAPE_R1 is bit-identical to
+    rt_sparse_attn_reshape; R2 on the calibration inputs gives dense attention
+    (the calibration identity, which both readings satisfy)."""
+    say("r1 through ex; r2 calibration identity")
+    cfg = small_cfg("pixart1024", H=4)
+    sh = rettn.shape_of(cfg)
+    (q0, k0, v0), (q1, k1, v1) = gu.gpu_inputs(cfg, 2, seed=21)
+    idx, _ = gu.select(sh, q0, k0, configs.forced_blocks(cfg))
+    cache = rettn.StatsCache(sh, 1)
+    gu.calibrate(sh, q0, k0, v0, idx, cache)
+    a = gu.sparse(sh, q1, k1, v1, cache)
+    b = gu.sparse(sh, q1, k1, v1, cache, variant="r1")
+    o2 = gu.sparse(sh, q0, k0, v0, cache, variant="r2")
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    gu.assert_close(gu.host(o2), oracle.dense_attention(gu.host(q0), gu.host(k0), gu.host(v0), cfg["N"], cfg["d"]))
+    cache.close()
 
 
 def test_bf16_residual_is_rounded_f32():
@@ -330,8 +381,9 @@ def test_sparse_kernel_with_oracle_cache(name):
     (130, 64, 64, 2, [0], "f32"),
     (333, 72, 80, 2, [], "f32"),
 ])
-def test_edge_shapes(N, d, D, keep, forced, dtype):
-    say("edge", N, d, D, keep, forced, dtype)
+@pytest.mark.parametrize("variant", ["r1", "r2"])
+def test_edge_shapes(N, d, D, keep, forced, dtype, variant):
+    say("edge", N, d, D, keep, forced, dtype, variant)
     B, H = 2, 3
     q0, k0, v0 = synth.random_qkv(B, H, N, d, D, seed=N + d, scale=1.5, dtype=dtype, device=gu.DEV)
     q1, k1, v1 = synth.random_qkv(B, H, N, d, D, seed=N + d + 1, scale=1.5, dtype=dtype, device=gu.DEV)
@@ -340,10 +392,10 @@ def test_edge_shapes(N, d, D, keep, forced, dtype):
     idx, _ = gu.select(sh, q0, k0, forced)
     cache = rettn.StatsCache(sh, 1)
     o_cal = gu.calibrate(sh, q0, k0, v0, torch.as_tensor(ref_idx).to(gu.DEV), cache)
-    o = gu.sparse(sh, q1, k1, v1, cache)
+    o = gu.sparse(sh, q1, k1, v1, cache, variant=variant)
     torch.cuda.synchronize()
     ref_cal = oracle.calibrate(gu.host(q0), gu.host(k0), gu.host(v0), ref_idx, N, d)
-    ref = oracle.sparse_reshape(gu.host(q1), gu.host(k1), gu.host(v1), ref_idx, ref_cal, N, d)
+    ref = oracle_layer(variant)(gu.host(q1), gu.host(k1), gu.host(v1), ref_idx, ref_cal, N, d)
     tol = dict(max_rel=1e-5, l1_rel=1e-6) if dtype == "f32" else {}
     gu.assert_close(gu.host(o_cal), ref_cal["o"], what="calibrate", **tol)
     gu.assert_close(gu.host(o), ref, what="sparse", **tol)
@@ -353,15 +405,15 @@ def test_edge_shapes(N, d, D, keep, forced, dtype):
     assert np.array_equal(idx.cpu().numpy(), ref_idx)
 
 
-@pytest.mark.parametrize("keep", [1, 2, 3, 9])
-def test_sparse_many_blocks_per_workgroup(keep):
+@pytest.mark.parametrize("keep,variant", [(1, "r1"), (2, "r1"), (3, "r1"), (9, "r1"), (1, "r2"), (9, "r2")])
+def test_sparse_many_blocks_per_workgroup(keep, variant):
     """The sparse kernel where each persistent workgroup walks several query
     blocks (so the prefetch of the next block's tiles, lists and rows crosses
     block boundaries), against the oracle's reshape on sampled query blocks.
     The statistics cache is synthetic: any positive Z_full >= Z_sparse, any m
     and any R give a well-defined reshape, and m spans values far below and
     above the new scores (exercising the lazy max from the cached reference)."""
-    say("sparse many blocks per workgroup", keep)
+    say("sparse many blocks per workgroup", keep, variant)
     B, H, d = 2, 16, 64
     N = 64 * 170 + 23  # ragged last block
     nb = (N + 63) // 64
@@ -389,7 +441,7 @@ def test_sparse_many_blocks_per_workgroup(keep):
     t["R"].copy_(torch.as_tensor(r_c, dtype=torch.float32))
     t["idx"].copy_(torch.as_tensor(idx))
     cache.set_valid(0)
-    o = gu.sparse(sh, q, k, v, cache)
+    o = gu.sparse(sh, q, k, v, cache, variant=variant)
     torch.cuda.synchronize()
     # the oracle reads the statistics as stored (float32)
     m32, zf32, zs32, r32 = (x.astype(np.float32) for x in (m_c, z_f, z_s, r_c))
@@ -399,9 +451,9 @@ def test_sparse_many_blocks_per_workgroup(keep):
         for h in range(H):
             for a in list(g.choice(nb - 1, 3, replace=False)) + [nb - 1]:
                 rows = slice(64 * a, min(64 * a + 64, N))
-                ref.append(oracle.sparse_reshape_rows(qh[b, h], kh[b, h], vh[b, h], rows, idx[b, h, a],
-                                                      m32[b, h, rows], zf32[b, h, rows], zs32[b, h, rows],
-                                                      r32[b, h, rows], N, d))
+                st = {"m": m32[b, h, rows], "z_full": zf32[b, h, rows], "z_sparse": zs32[b, h, rows]}
+                ref.append(oracle_rows(variant, qh[b, h], kh[b, h], vh[b, h], rows, idx[b, h, a], st,
+                                       r32[b, h, rows], N, d))
                 got.append(oh[b, h, rows])
     gu.assert_close(np.concatenate(got), np.concatenate(ref))
 
