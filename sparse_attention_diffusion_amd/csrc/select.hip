@@ -13,7 +13,8 @@
 //                   are read once); float32 partial sums per row group are
 //                   reduced through LDS.  K means are written transposed
 //                   ([bh][d][block]) so that scoring reads them coalesced.
-//   select_kernel : one wave per (bh, QG query blocks).  Lane j scores key
+//   select_kernel : one wave per (bh, QG = 8 query blocks; 4 above 512 key
+//                   blocks).  Lane j scores key
 //                   blocks j, j+64, ... against the QG pooled queries (float32
 //                   dot products in ascending d), then each query block's
 //                   keep - n_forced winners are taken by rounds of a wave-wide
@@ -118,8 +119,27 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x)
   return x;
 }
 
-constexpr int kQG = 4;          // query blocks per wave
 constexpr int kMaxRounds = 32;  // above this many non-forced winners: bitonic sort
+
+// Query blocks per wave: 8 while the per-lane scores fit in registers.
+template <int CH>
+constexpr int query_group() { return CH <= 8 ? 8 : 4; }
+
+// Dynamic LDS of select_kernel: pooled queries [QG][D] floats, flag rows
+// [QG][Nb rounded up to 4] bytes, and (bitonic fallback only) P 64-bit keys.
+struct SelectLds {
+  int flag_stride, keys_off, bytes;
+};
+inline SelectLds select_lds(int QG, int D, int Nb, bool bitonic) {
+  SelectLds l;
+  l.flag_stride = (Nb + 3) & ~3;
+  const int flags_off = QG * D * 4;
+  l.keys_off = (flags_off + QG * l.flag_stride + 7) & ~7;
+  int P = 64;
+  while (P < Nb) P <<= 1;
+  l.bytes = l.keys_off + (bitonic ? P * 8 : 0);
+  return l;
+}
 
 // Writes the kept list of one query block from its flag row (ascending).
 __device__ __forceinline__ void emit(const unsigned char* flags, int Nb, int32_t* out) {
@@ -136,60 +156,67 @@ __device__ __forceinline__ void emit(const unsigned char* flags, int Nb, int32_t
 
 // CH: key blocks per lane (64-block chunks), at least ceil(Nb / 64).
 template <int D, int CH>
-__global__ void __launch_bounds__(64) select_kernel(SelectArgs a, XcdGrid grid) {
-  __shared__ __attribute__((aligned(16))) float qrow[kQG][D];
-  __shared__ unsigned char flags[kQG][kMaxBlocks];
-  __shared__ unsigned long long keys[kMaxBlocks];
+__global__ void __launch_bounds__(64) select_kernel(SelectArgs a, XcdGrid grid, SelectLds lay) {
+  constexpr int QG = query_group<CH>();
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float(*qrow)[D] = (float(*)[D])smem;
+  unsigned char* flag0 = (unsigned char*)smem + QG * D * 4;
+  unsigned long long* keys = (unsigned long long*)(smem + lay.keys_off);
 
   const uint32_t lin = grid.linear(blockIdx.x);
   if (lin >= grid.total) return;
   const int Nb = a.Nb, keep = a.keep;
-  const int groups = (Nb + kQG - 1) / kQG;
-  const int bh = lin / groups, i0 = (lin % groups) * kQG;
-  const int nq = min(kQG, Nb - i0);
+  const int groups = (Nb + QG - 1) / QG;
+  const int bh = lin / groups, i0 = (lin % groups) * QG;
+  const int nq = min(QG, Nb - i0);
   const int lane = threadIdx.x;
-  for (int e = lane; e < kQG * D; e += 64) {
+  for (int e = lane; e < QG * D; e += 64) {
     const int g = e / D, d = e % D;
     qrow[g][d] = g < nq ? a.qb[((size_t)bh * Nb + i0 + g) * D + d] : 0.f;
   }
-  for (int e = lane; e < kQG * kMaxBlocks; e += 64) (&flags[0][0])[e] = 0;
+  for (int e = lane; e < QG * lay.flag_stride / 4; e += 64) ((uint32_t*)flag0)[e] = 0u;
   int n_forced = 0;
 #pragma unroll
   for (int w = 0; w < kMaxBlocks / 32; ++w) n_forced += __popc(a.forced[w]);
   __syncthreads();
 
-  // Scores of key blocks j = lane + 64c against the kQG pooled queries.
+  // Scores of key blocks j = lane + 64c against the QG pooled queries: float32
+  // products summed in ascending d; the K means of 16 d at a time are loaded
+  // together.
   const float* kt = a.kb + (size_t)bh * D * Nb;  // transposed means [d][j]
   const int nc = (Nb + 63) / 64;
-  float sc[kQG][CH];
+  float sc[QG][CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     if (c < nc) {
-      const int j = c * 64 + lane;
-      const int jj = min(j, Nb - 1);
-      float acc[kQG];
+      const int jj = min(c * 64 + lane, Nb - 1);
+      float acc[QG];
 #pragma unroll
-      for (int g = 0; g < kQG; ++g) acc[g] = 0.f;
-      for (int d = 0; d < D; d += 4) {
-        float kv[4];
+      for (int g = 0; g < QG; ++g) acc[g] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) kv[e] = kt[(size_t)(d + e) * Nb + jj];
+      for (int d0 = 0; d0 < D; d0 += 16) {
+        float kv[16];
 #pragma unroll
-        for (int g = 0; g < kQG; ++g) {
-          const f32x4 qv = *(const f32x4*)&qrow[g][d];
+        for (int e = 0; e < 16; ++e) kv[e] = kt[(size_t)(d0 + e) * Nb + jj];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[g] = fmaf(qv[e], kv[e], acc[g]);
-        }
+        for (int e4 = 0; e4 < 16; e4 += 4)
+#pragma unroll
+          for (int g = 0; g < QG; ++g) {
+            const f32x4 qv = *(const f32x4*)&qrow[g][d0 + e4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[g] = fmaf(qv[e], kv[e4 + e], acc[g]);
+          }
       }
 #pragma unroll
-      for (int g = 0; g < kQG; ++g) sc[g][c] = acc[g] * a.alpha + 0.0f;  // + 0: -0 -> +0
+      for (int g = 0; g < QG; ++g) sc[g][c] = acc[g] * a.alpha + 0.0f;  // + 0: -0 -> +0
     }
   }
 
 #pragma unroll
-  for (int g = 0; g < kQG; ++g) {
+  for (int g = 0; g < QG; ++g) {
     if (g >= nq) break;
     const int i = i0 + g;
+    unsigned char* flags = flag0 + g * lay.flag_stride;
     if (a.scores) {
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
@@ -205,7 +232,7 @@ __global__ void __launch_bounds__(64) select_kernel(SelectArgs a, XcdGrid grid) 
       const int j = c * 64 + lane;
       kk[c] = 0ull;
       if (c < nc && j < Nb) {
-        if ((a.forced[j >> 5] >> (j & 31)) & 1u) flags[g][j] = 1;
+        if ((a.forced[j >> 5] >> (j & 31)) & 1u) flags[j] = 1;
         else kk[c] = ((unsigned long long)order_key(sc[g][c]) << 32) | (0xFFFFFFFFu - (uint32_t)j);
       }
     }
@@ -219,7 +246,7 @@ __global__ void __launch_bounds__(64) select_kernel(SelectArgs a, XcdGrid grid) 
         if (best == 0ull) break;  // no candidate left (more rounds than blocks)
         const int jw = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
         if (lane == (jw & 63)) {
-          flags[g][jw] = 1;
+          flags[jw] = 1;
 #pragma unroll
           for (int c = 0; c < CH; ++c)
             if (c == (jw >> 6)) kk[c] = 0ull;
@@ -248,11 +275,21 @@ __global__ void __launch_bounds__(64) select_kernel(SelectArgs a, XcdGrid grid) 
           __syncthreads();
         }
       }
-      for (int t = lane; t < rounds; t += 64) flags[g][0xFFFFFFFFu - (uint32_t)(keys[t] & 0xFFFFFFFFull)] = 1;
+      for (int t = lane; t < rounds; t += 64) flags[0xFFFFFFFFu - (uint32_t)(keys[t] & 0xFFFFFFFFull)] = 1;
     }
     __syncthreads();
-    emit(flags[g], Nb, a.idx + ((size_t)bh * Nb + i) * keep);
+    emit(flags, Nb, a.idx + ((size_t)bh * Nb + i) * keep);
   }
+}
+
+template <int D, int CH>
+void launch_select_ch(const SelectArgs& a, hipStream_t s) {
+  constexpr int QG = query_group<CH>();
+  int n_forced = 0;
+  for (int w = 0; w < kMaxBlocks / 32; ++w) n_forced += __builtin_popcount(a.forced[w]);
+  const SelectLds lay = select_lds(QG, D, a.Nb, a.keep - n_forced > kMaxRounds);
+  XcdGrid sg = make_xcd_grid((uint32_t)a.BH * (uint32_t)((a.Nb + QG - 1) / QG));
+  hipLaunchKernelGGL((select_kernel<D, CH>), dim3(sg.grid()), dim3(64), lay.bytes, s, a, sg, lay);
 }
 
 template <typename T, int D>
@@ -261,13 +298,13 @@ hipError_t launch_typed(const SelectArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((pool_kernel<T, D>), dim3(pg.grid(), 2), dim3(64), 0, s, a, pg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  XcdGrid sg = make_xcd_grid((uint32_t)a.BH * (uint32_t)((a.Nb + kQG - 1) / kQG));
   const int nc = (a.Nb + 63) / 64;
-  if (nc <= 1) hipLaunchKernelGGL((select_kernel<D, 1>), dim3(sg.grid()), dim3(64), 0, s, a, sg);
-  else if (nc <= 2) hipLaunchKernelGGL((select_kernel<D, 2>), dim3(sg.grid()), dim3(64), 0, s, a, sg);
-  else if (nc <= 4) hipLaunchKernelGGL((select_kernel<D, 4>), dim3(sg.grid()), dim3(64), 0, s, a, sg);
-  else if (nc <= 8) hipLaunchKernelGGL((select_kernel<D, 8>), dim3(sg.grid()), dim3(64), 0, s, a, sg);
-  else hipLaunchKernelGGL((select_kernel<D, kMaxBlocks / 64>), dim3(sg.grid()), dim3(64), 0, s, a, sg);
+  if (nc <= 1) launch_select_ch<D, 1>(a, s);
+  else if (nc <= 2) launch_select_ch<D, 2>(a, s);
+  else if (nc <= 4) launch_select_ch<D, 4>(a, s);
+  else if (nc <= 5) launch_select_ch<D, 5>(a, s);
+  else if (nc <= 8) launch_select_ch<D, 8>(a, s);
+  else launch_select_ch<D, kMaxBlocks / 64>(a, s);
   return hipGetLastError();
 }
 
