@@ -182,6 +182,12 @@ def components(cfg, reps=20, flush_mb=512):
     torch.cuda.synchronize()
     t2w, _ = timed(spa2, reps)
     t2c, _ = timed(spa2, reps, cold=True)
+    # a sparse step with per-step reselection (selector, then the sparse kernel on the new lists)
+    wss = torch.empty(rettn.step_workspace_bytes(sh), dtype=torch.uint8, device=dev)
+    rsel = lambda: rettn.rt_attention_step_ex(sh, q1, k1, v1, forced, cache, 0, 1, 0, "r1", True, out, wss)
+    rsel()
+    torch.cuda.synchronize()
+    t_rsel, _ = timed(rsel, reps)
     # the same with the residual cached in bf16 (cache option; float32 is the baseline)
     t16w = t16c = None
     if cfg["dtype"] == "bf16":
@@ -215,6 +221,7 @@ def components(cfg, reps=20, flush_mb=512):
         "sparse_bf16_residual_alg_bytes": None if t16w is None else byts - sh.B * sh.H * N * D * 2,
         "sparse_r2_warm_ms": round(t2w, 5), "sparse_r2_cold_ms": round(t2c, 5),
         "sparse_r2_alg_bytes": byts - sh.B * sh.H * N * 4,  # no cached row max
+        "sparse_step_reselect_ms": round(t_rsel, 5),
     }
     cache.close()
     return res
@@ -231,7 +238,9 @@ def fidelity(cfg, period):
         step-0 cache with Z_sparse = Z_full and R = 0 makes both epilogues
         compute exactly that);
       * R1 and R2 from the step-0 cache (one calibration, lists fixed);
-      * R1 and R2 with recalibration (fresh lists) every `period` steps.
+      * R1 and R2 with recalibration (fresh lists) every `period` steps;
+      * plain sparse, R1 and R2 with the lists reselected on every step's q and
+        k and the step-0 statistics (rt_attention_step_ex with reselection).
     Also per step: the median and 90th percentile over rows of |r_t/r_0 - 1|
     and of |m_t - m_0| (cached row max, logit units) for the fixed mask."""
     import numpy as np
@@ -246,6 +255,7 @@ def fidelity(cfg, period):
     it = synth.StepInputs(cfg, seed=0, device=dev)
     c0, cdense, cplain, cper = (rettn.StatsCache(sh, 1, device=dev) for _ in range(4))
     idx = torch.empty((sh.B, sh.H, nb, keep), dtype=torch.int32, device=dev)
+    idx_t = torch.empty_like(idx)
     ws = torch.empty(rettn.select_workspace_bytes(sh), dtype=torch.uint8, device=dev)
     new = lambda: torch.empty((sh.B, sh.H, N, D), dtype=rettn.torch_dtype(sh), device=dev)
     o_dense, o = new(), new()
@@ -279,6 +289,13 @@ def fidelity(cfg, period):
         rec = {"step": s, "r_drift_p50": qr[0], "r_drift_p90": qr[1], "m_drift_p50": qm[0], "m_drift_p90": qm[1]}
         rettn.rt_sparse_attn_reshape_ex(sh, q, k, v, None, cplain, 0, "r2", o)
         rec["plain"] = err(o, o_dense)
+        rettn.rt_select_blocks(sh, q, k, forced, idx_t, None, ws)
+        rettn.rt_sparse_attn_reshape_ex(sh, q, k, v, idx_t, cplain, 0, "r2", o)
+        rec["plain_resel"] = err(o, o_dense)
+        for var in ("r1", "r2"):
+            rettn.rt_sparse_attn_reshape_ex(sh, q, k, v, idx_t, c0, 0, var, o)
+            rec[var + "_resel"] = err(o, o_dense)
+        rec["lists_changed"] = float((idx_t != t0["idx"]).any(dim=-1).float().mean())
         for var in ("r1", "r2"):
             rettn.rt_sparse_attn_reshape_ex(sh, q, k, v, None, c0, 0, var, o)
             rec[var] = err(o, o_dense)

@@ -205,6 +205,26 @@ rt_status rt_attention_step(const rt_shape* shape, const void* q, const void* k,
                             void* workspace, size_t workspace_bytes, void* stream,
                             int32_t* did_calibrate);
 
+/* The same schedule with a choice of reshape (`variant`, RT_RESHAPE_R1 or
+ * RT_RESHAPE_R2) and `flags`:
+ *   RT_STEP_RESELECT: on sparse steps too, run rt_select_blocks on this step's
+ *     q and k (into the workspace) and attend to those lists instead of the
+ *     cached ones.  The cached statistics still describe the calibration
+ *     step's masked set, so where the lists differ the reshape is an
+ *     approximation: this library applies the same formula with the new kept
+ *     set (the pages state no rule for a changing mask).  The cached lists
+ *     are not replaced.
+ * Unknown flag bits or variants are RT_E_ARG.  rt_attention_step(...) is
+ * rt_attention_step_ex(..., RT_RESHAPE_R1, 0, ...).  The workspace is
+ * rt_step_workspace_bytes either way; with RT_STEP_RESELECT it is used on
+ * every step.                                                               */
+enum { RT_STEP_RESELECT = 1 };
+rt_status rt_attention_step_ex(const rt_shape* shape, const void* q, const void* k, const void* v,
+                               const int32_t* forced, int32_t n_forced, rt_stats_cache* cache,
+                               int32_t layer, int32_t step, int32_t period, int32_t variant,
+                               int32_t flags, void* o, void* workspace, size_t workspace_bytes,
+                               void* stream, int32_t* did_calibrate);
+
 #ifdef __cplusplus
 }
 #endif

@@ -390,21 +390,39 @@ size_t rt_step_workspace_bytes(const rt_shape* s) {
 rt_status rt_attention_step(const rt_shape* s, const void* q, const void* k, const void* v, const int32_t* forced,
                             int32_t n_forced, rt_stats_cache* c, int32_t layer, int32_t step, int32_t period,
                             void* o, void* workspace, size_t ws_bytes, void* stream, int32_t* did_calibrate) {
+  return rt_attention_step_ex(s, q, k, v, forced, n_forced, c, layer, step, period, RT_RESHAPE_R1, 0, o, workspace,
+                              ws_bytes, stream, did_calibrate);
+}
+
+rt_status rt_attention_step_ex(const rt_shape* s, const void* q, const void* k, const void* v,
+                               const int32_t* forced, int32_t n_forced, rt_stats_cache* c, int32_t layer,
+                               int32_t step, int32_t period, int32_t variant, int32_t flags, void* o,
+                               void* workspace, size_t ws_bytes, void* stream, int32_t* did_calibrate) {
+  if (did_calibrate != nullptr) *did_calibrate = 0;
   rt_status st = check_shape(s);
   if (st != RT_OK) return st;
   if ((st = check_cache(s, c, layer)) != RT_OK) return st;
   if (step < 0) return fail(RT_E_ARG, "step must be >= 0 (got %d)", step);
+  if (variant != RT_RESHAPE_R1 && variant != RT_RESHAPE_R2)
+    return fail(RT_E_ARG, "reshape variant must be RT_RESHAPE_R1 or RT_RESHAPE_R2 (got %d)", variant);
+  if ((flags & ~RT_STEP_RESELECT) != 0) return fail(RT_E_ARG, "unknown step flags 0x%x", (unsigned)flags);
   const bool calib = rt_schedule_is_calibration(step, period) != 0;
+  const bool reselect = (flags & RT_STEP_RESELECT) != 0;
+  if (!calib && !c->valid[layer]) return fail(RT_E_STATE, "layer %d has no valid statistics (calibrate first)", layer);
   if (did_calibrate != nullptr) *did_calibrate = calib ? 1 : 0;
-  if (!calib) return rt_sparse_attn_reshape(s, q, k, v, nullptr, c, layer, o, stream);
-  if (is_empty(s)) return rt_calibrate(s, q, k, v, nullptr, c, layer, o, stream);
+  if (!calib && !reselect) return rt_sparse_attn_reshape_ex(s, q, k, v, nullptr, c, layer, variant, o, stream);
+  if (is_empty(s)) {
+    return calib ? rt_calibrate(s, q, k, v, nullptr, c, layer, o, stream)
+                 : rt_sparse_attn_reshape_ex(s, q, k, v, nullptr, c, layer, variant, o, stream);
+  }
   if (workspace == nullptr) return fail(RT_E_ARG, "workspace is NULL");
   if (ws_bytes < rt_step_workspace_bytes(s))
     return fail(RT_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, rt_step_workspace_bytes(s));
   int32_t* lists = (int32_t*)((char*)workspace + select_ws(s));
   st = rt_select_blocks(s, q, k, forced, n_forced, lists, nullptr, workspace, select_ws(s), stream);
   if (st != RT_OK) return st;
-  return rt_calibrate(s, q, k, v, lists, c, layer, o, stream);
+  if (calib) return rt_calibrate(s, q, k, v, lists, c, layer, o, stream);
+  return rt_sparse_attn_reshape_ex(s, q, k, v, lists, c, layer, variant, o, stream);
 }
 
 }  // extern "C"

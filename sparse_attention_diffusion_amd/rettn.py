@@ -61,6 +61,8 @@ def _load():
         "rt_step_workspace_bytes": (SZ, [S]),
         "rt_attention_step": (I32, [S, P, P, P, ctypes.POINTER(I32), I32, P, I32, I32, I32, P, P, SZ, P,
                                     ctypes.POINTER(I32)]),
+        "rt_attention_step_ex": (I32, [S, P, P, P, ctypes.POINTER(I32), I32, P, I32, I32, I32, I32, I32, P, P, SZ,
+                                       P, ctypes.POINTER(I32)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -76,6 +78,7 @@ SYMBOLS = [
     "rt_stats_cache_init_ex", "rt_stats_cache_view",
     "rt_stats_cache_set_valid", "rt_stats_cache_invalidate", "rt_stats_cache_destroy", "rt_calibrate",
     "rt_sparse_attn_reshape", "rt_sparse_attn_reshape_ex", "rt_schedule_is_calibration", "rt_step_workspace_bytes", "rt_attention_step",
+    "rt_attention_step_ex",
 ]
 
 
@@ -224,6 +227,7 @@ def rt_sparse_attn_reshape(sh, q, k, v, block_idx, cache, layer, o, stream=None)
 
 
 RT_RESHAPE_R1, RT_RESHAPE_R2 = 0, 1
+RT_STEP_RESELECT = 1
 _VARIANTS = {"r1": RT_RESHAPE_R1, "r2": RT_RESHAPE_R2}
 
 
@@ -243,4 +247,20 @@ def rt_attention_step(sh, q, k, v, forced, cache, layer, step, period, o, worksp
                                   cache.handle, layer, step, period, _ptr(o), _ptr(workspace),
                                   0 if workspace is None else workspace.numel() * workspace.element_size(),
                                   _stream(stream), ctypes.byref(did)))
+    return bool(did.value)
+
+
+def rt_attention_step_ex(sh, q, k, v, forced, cache, layer, step, period, variant, reselect, o, workspace,
+                         stream=None):
+    """rt_attention_step with a reshape variant ("r1" / "r2") and per-step reselection."""
+    var = _VARIANTS.get(variant, variant) if isinstance(variant, str) else int(variant)
+    if isinstance(var, str):
+        raise ValueError(f"unknown reshape variant {variant!r}")
+    arr, n = _forced_arr(forced)
+    did = ctypes.c_int32(0)
+    _check(_lib.rt_attention_step_ex(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), arr if n else None, n,
+                                     cache.handle, layer, step, period, var, RT_STEP_RESELECT if reselect else 0,
+                                     _ptr(o), _ptr(workspace),
+                                     0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                     _stream(stream), ctypes.byref(did)))
     return bool(did.value)

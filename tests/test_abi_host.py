@@ -206,6 +206,12 @@ def test_state_machine_without_gpu():
     st = lib.rt_attention_step(ctypes.byref(sh), p, p, p, None, 0, h, 0, 3, 10, p, p, 1 << 20, None,
                                ctypes.byref(did))
     assert st == rettn.RT_E_STATE and did.value == 0
+    for var, flags, want in ((0, 0, rettn.RT_E_STATE), (1, 1, rettn.RT_E_STATE), (2, 0, rettn.RT_E_ARG),
+                             (0, 2, rettn.RT_E_ARG), (0, -1, rettn.RT_E_ARG)):
+        did = ctypes.c_int32(-1)
+        st = lib.rt_attention_step_ex(ctypes.byref(sh), p, p, p, None, 0, h, 0, 3, 10, var, flags, p, p, 1 << 20,
+                                      None, ctypes.byref(did))
+        assert st == want and did.value == 0, (var, flags, st)
     lib.rt_stats_cache_destroy(h)
     del buf
 

@@ -503,6 +503,43 @@ def test_schedule_pixart512_through_attention_step():
         gu.assert_close(gu.host(o), ref, what=f"step {s}")
 
 
+@pytest.mark.parametrize("variant", ["r1", "r2"])
+def test_schedule_with_reselection(variant):
+    """rt_attention_step_ex with per-step reselection: every step's lists are
+    the selector's on that step's q and k (compared with the oracle's), the
+    cached statistics stay those of step 0, and each sparse step equals the
+    oracle's reshape over the new lists."""
+    say("schedule pixart512 reselect", variant)
+    cfg = configs.CONFIGS["pixart512"]
+    sh = rettn.shape_of(cfg)
+    N, d, keep = cfg["N"], cfg["d"], cfg["keep"]
+    nb = configs.n_blocks(N)
+    stepsin = gu.gpu_inputs(cfg, 4, seed=17)
+    cache = rettn.StatsCache(sh, 1)
+    ws = torch.empty(rettn.step_workspace_bytes(sh), dtype=torch.uint8, device=gu.DEV)
+    off = rettn.select_workspace_bytes(sh)
+    ref_cal, changed = None, False
+    for s, (q, k, v) in enumerate(stepsin):
+        o = gu.empty_out(sh)
+        did = rettn.rt_attention_step_ex(sh, q, k, v, [], cache, 0, s, 0, variant, True, o, ws)
+        torch.cuda.synchronize()
+        assert did == (s == 0)
+        ref_idx = gu.oracle_lists(cfg, q, k, [], keep)
+        got_idx = ws[off: off + sh.B * sh.H * nb * keep * 4].view(torch.int32).cpu().numpy()
+        assert np.array_equal(got_idx.reshape(ref_idx.shape), ref_idx), f"step {s} lists"
+        if s == 0:
+            ref_cal = oracle.calibrate(gu.host(q), gu.host(k), gu.host(v), ref_idx, N, d)
+            ref = ref_cal["o"]
+            cal_idx = ref_idx
+        else:
+            assert np.array_equal(cache.tensors(0)["idx"].cpu().numpy(), cal_idx)  # cache keeps step 0's lists
+            ref = oracle_layer(variant)(gu.host(q), gu.host(k), gu.host(v), ref_idx, ref_cal, N, d)
+            changed = changed or not np.array_equal(ref_idx, cal_idx)
+        gu.assert_close(gu.host(o), ref, what=f"step {s}")
+    assert changed  # the lists did move, so reselection was exercised
+    cache.close()
+
+
 def test_cogvideox5b_layers_and_recalibration():
     """42 layers share one cache allocation; layers 0 and 41 run a 12-step
     schedule with recalibration every 10 steps; sampled rows of the
