@@ -4,6 +4,7 @@ TEST INFRASTRUCTURE ONLY.  Nothing in the library imports this package; only
 the test-suite, the smoke check and the CPU-baseline leg of the benchmark do.
 It shares no code with the HIP path.
 """
+from . import hilbert  # noqa: F401
 from .rettention import (  # noqa: F401
     BLOCK,
     block_ranges,
