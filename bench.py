@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--fidelity", action="store_true",
                    help="reshape fidelity study over the denoising schedule (one JSON line; not the headline)")
     p.add_argument("--period", type=int, default=10, help="recalibration period of the --fidelity study")
+    p.add_argument("--order", choices=["raster", "hilbert"], default="raster",
+                   help="token order of --fidelity and --all-configs (hilbert: rt_hilbert_order + rt_permute_rows "
+                        "on the inputs)")
     return p.parse_args()
 
 
@@ -126,7 +129,21 @@ def cpu_baseline(cfg, heads, budget_s):
     }
 
 
-def components(cfg, reps=20, flush_mb=512):
+def hilbert_reorder(cfg, sh, dev):
+    """Device permutation of the workload's Hilbert order and a function that
+    reorders one [B,H,N,d_pad] tensor with it (rt_permute_rows)."""
+    import torch
+    from sparse_attention_diffusion_amd import rettn
+    perm = torch.as_tensor(rettn.rt_hilbert_order(cfg["grid"][1:], cfg["n_text"])).to(dev)
+
+    def apply(t):
+        out = torch.empty_like(t)
+        rettn.rt_permute_rows(sh, t, out, perm)
+        return out
+    return perm, apply
+
+
+def components(cfg, reps=20, flush_mb=512, order="raster"):
     """Per-kernel breakdown on one configuration, from step-0 and step-1 inputs:
     the selector (rt_select_blocks) with its HBM bytes, the calibration kernel
     with its dense FLOPs, and the sparse kernel warm (the same inputs call after
@@ -143,6 +160,21 @@ def components(cfg, reps=20, flush_mb=512):
     it = synth.StepInputs(cfg, seed=0, device=dev)
     (q0, k0, v0), (q1, k1, v1) = [tuple(synth.store(x, cfg["dtype"]) for x in it.next()) for _ in range(2)]
     del it
+    perm_ms = None
+    if order == "hilbert":
+        perm, reorder = hilbert_reorder(cfg, sh, dev)
+        q0, k0, v0, q1, k1, v1 = (reorder(t) for t in (q0, k0, v0, q1, k1, v1))
+        tmp = torch.empty_like(q0)
+        pm = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rettn.rt_permute_rows(sh, q0, tmp, perm)
+            e1.record()
+            e1.synchronize()
+            pm.append(e0.elapsed_time(e1))
+        perm_ms = float(np.median(pm))
+        del tmp
     ebytes = 2 if cfg["dtype"] == "bf16" else 4
     nb = configs.n_blocks(N)
     idx = torch.empty((sh.B, sh.H, nb, keep), dtype=torch.int32, device=dev)
@@ -200,12 +232,18 @@ def components(cfg, reps=20, flush_mb=512):
         t16c, _ = timed(spa16, reps, cold=True)
         c16.close()
     lists = idx.cpu().numpy()
+    nf = len(forced)
+    qi = np.arange(nb)[None, None, :, None]
+    dist = np.abs(lists - qi)
+    free = np.ones_like(lists, dtype=bool) if nf == 0 else ~np.isin(lists, forced)
     flop = kept_flops(lists, N, d)
     byts = sparse_call_bytes(lists, N, D, ebytes)
     dense = 4 * d * N * N * sh.B * sh.H
     sel_bytes = 2 * sh.B * sh.H * N * D * ebytes  # Q and K read once
     res = {
         "config": cfg["name"] if "name" in cfg else None,
+        "order": order,
+        "lists_median_block_distance": float(np.median(dist[free])),
         "select_ms": round(t_sel, 4), "select_hbm_gbs": round(sel_bytes / (t_sel * 1e-3) / 1e9, 1),
         "calibrate_ms": round(t_cal, 4), "calibrate_tflops": round(dense / (t_cal * 1e-3) / 1e12, 1),
         "calibrate_mfma_frac": round(dense / (t_cal * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -222,12 +260,14 @@ def components(cfg, reps=20, flush_mb=512):
         "sparse_r2_warm_ms": round(t2w, 5), "sparse_r2_cold_ms": round(t2c, 5),
         "sparse_r2_alg_bytes": byts - sh.B * sh.H * N * 4,  # no cached row max
         "sparse_step_reselect_ms": round(t_rsel, 5),
+        "permute_ms": None if perm_ms is None else round(perm_ms, 5),
+        "permute_gbs": None if perm_ms is None else round(2 * sh.B * sh.H * N * D * ebytes / (perm_ms * 1e-3) / 1e9, 1),
     }
     cache.close()
     return res
 
 
-def fidelity(cfg, period):
+def fidelity(cfg, period, order="raster"):
     """How close each sparse step is to dense attention over a denoising
     schedule, on the GPU path alone.  Dense attention of every step comes from
     rt_calibrate (its output is dense attention; a second cache is recalibrated
@@ -253,6 +293,7 @@ def fidelity(cfg, period):
     forced = configs.forced_blocks(cfg)
     nb = configs.n_blocks(N)
     it = synth.StepInputs(cfg, seed=0, device=dev)
+    reorder = hilbert_reorder(cfg, sh, dev)[1] if order == "hilbert" else (lambda t: t)
     c0, cdense, cplain, cper = (rettn.StatsCache(sh, 1, device=dev) for _ in range(4))
     idx = torch.empty((sh.B, sh.H, nb, keep), dtype=torch.int32, device=dev)
     idx_t = torch.empty_like(idx)
@@ -264,7 +305,7 @@ def fidelity(cfg, period):
         a, ref = a.float(), ref.float()
         return float((a - ref).abs().sum() / ref.abs().sum())
 
-    q, k, v = (synth.store(x, cfg["dtype"]) for x in it.next())
+    q, k, v = (reorder(synth.store(x, cfg["dtype"])) for x in it.next())
     rettn.rt_select_blocks(sh, q, k, forced, idx, None, ws)
     rettn.rt_calibrate(sh, q, k, v, idx, c0, 0, o_dense)
     rettn.rt_calibrate(sh, q, k, v, idx, cper, 0, o_dense)
@@ -278,7 +319,7 @@ def fidelity(cfg, period):
     m0 = t0["m"].clone()
     rows = []
     for s in range(1, cfg["steps"]):
-        q, k, v = (synth.store(x, cfg["dtype"]) for x in it.next())
+        q, k, v = (reorder(synth.store(x, cfg["dtype"])) for x in it.next())
         rettn.rt_calibrate(sh, q, k, v, idx, cdense, 0, o_dense)
         td = cdense.tensors(0)
         dr = ((td["z_sparse"] / td["z_full"]) / r0 - 1).abs().flatten()
@@ -312,6 +353,7 @@ def fidelity(cfg, period):
     for c in (c0, cdense, cplain, cper):
         c.close()
     return {"study": "reshape fidelity vs dense attention", "config": cfg.get("name"), "period": period,
+            "order": order,
             "data": "synthetic drift inputs, seed 0", "metric": "L1(O - O_dense) / L1(O_dense) per step",
             "steps": rows}
 
@@ -337,13 +379,14 @@ def main():
     from sparse_attention_diffusion_amd import configs, rettn, synth
 
     if args.fidelity:
-        print(json.dumps(fidelity(dict(configs.CONFIGS[args.config], name=args.config), args.period)), flush=True)
+        print(json.dumps(fidelity(dict(configs.CONFIGS[args.config], name=args.config), args.period, args.order)),
+              flush=True)
         return
     if args.all_configs:
         torch.cuda.set_device(0)
         for name in configs.CONFIGS:
             c = dict(configs.CONFIGS[name], name=name)
-            print(json.dumps(components(c)), flush=True)
+            print(json.dumps(components(c, order=args.order)), flush=True)
         return
     cfg = dict(configs.CONFIGS[args.config])
     if args.denoise_steps:

@@ -225,6 +225,31 @@ rt_status rt_attention_step_ex(const rt_shape* shape, const void* q, const void*
                                int32_t flags, void* o, void* workspace, size_t workspace_bytes,
                                void* stream, int32_t* did_calibrate);
 
+/* ---- locality-preserving token order (HilbertA blog page, sections
+ * "Introducing HilbertA" and "Future Directions": tokens reordered along a 2-D
+ * or 3-D Hilbert curve so that grid neighbours stay close in the sequence; the
+ * reorder is done once before and once after the denoising loop) ----
+ *
+ * rt_hilbert_order (host only, no device call): fills perm[0..n) with
+ * n = n_text + dims[0]*...*dims[ndims-1].  perm[i] < n_text is i (text tokens
+ * first, unchanged); the grid tokens, numbered in raster order after the text
+ * with dims[0] the slowest axis ((y, x) or (t, y, x)), follow in the order of
+ * their index along the standard Hilbert curve of the smallest 2^k cube that
+ * encloses the grid (coordinates in the same axis order).  perm[i] is the
+ * original position of the token placed at i.  ndims must be 1..3 and every
+ * dims[a] >= 1 (RT_E_ARG); more than 65536 tokens is RT_E_SHAPE.            */
+rt_status rt_hilbert_order(const int32_t* dims, int32_t ndims, int32_t n_text, int32_t* perm, int32_t n);
+
+/* rt_permute_rows: reorders the rows of a [B,H,N,d_pad] tensor of shape->dtype.
+ * inverse = 0: dst[b,h,i,:] = src[b,h,perm[i],:] (into the new order);
+ * inverse = 1: dst[b,h,perm[i],:] = src[b,h,i,:] (back to the original order).
+ * perm: device int32 [N], a permutation of 0..N-1 (entries are clamped into
+ * range; a list that is not a permutation gives unspecified rows).  src and
+ * dst are device buffers that must not overlap (RT_E_ARG), 16-byte aligned.
+ * Asynchronous on `stream`.                                                 */
+rt_status rt_permute_rows(const rt_shape* shape, const void* src, void* dst, const int32_t* perm,
+                          int32_t inverse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -425,4 +425,49 @@ rt_status rt_attention_step_ex(const rt_shape* s, const void* q, const void* k, 
   return rt_sparse_attn_reshape_ex(s, q, k, v, lists, c, layer, variant, o, stream);
 }
 
+rt_status rt_hilbert_order(const int32_t* dims, int32_t ndims, int32_t n_text, int32_t* perm, int32_t n) {
+  if (dims == nullptr || perm == nullptr) return fail(RT_E_ARG, "dims or perm is NULL");
+  if (ndims < 1 || ndims > 3) return fail(RT_E_ARG, "ndims must be 1, 2 or 3 (got %d)", ndims);
+  if (n_text < 0) return fail(RT_E_ARG, "n_text must be >= 0 (got %d)", n_text);
+  int64_t count = 1;
+  for (int32_t a = 0; a < ndims; ++a) {
+    if (dims[a] < 1) return fail(RT_E_ARG, "dims[%d]=%d must be >= 1", a, dims[a]);
+    count *= dims[a];
+    if (count > 65536) return fail(RT_E_SHAPE, "grid of more than 65536 tokens");
+  }
+  if ((int64_t)n != (int64_t)n_text + count)
+    return fail(RT_E_ARG, "n=%d but n_text + prod(dims) = %lld", n, (long long)(n_text + count));
+  if (n > 65536) return fail(RT_E_SHAPE, "N=%d exceeds 65536", n);
+  rettn::hilbert_order(dims, ndims, n_text, perm);
+  return RT_OK;
+}
+
+rt_status rt_permute_rows(const rt_shape* s, const void* src, void* dst, const int32_t* perm, int32_t inverse,
+                          void* stream) {
+  rt_status st = check_shape(s);
+  if (st != RT_OK) return st;
+  if (inverse != 0 && inverse != 1) return fail(RT_E_ARG, "inverse must be 0 or 1 (got %d)", inverse);
+  if (is_empty(s)) return RT_OK;
+  const void* ptrs[] = {src, dst};
+  const char* names[] = {"src", "dst"};
+  if ((st = check_tensors(ptrs, names, 2)) != RT_OK) return st;
+  if (perm == nullptr || (reinterpret_cast<uintptr_t>(perm) & 3u)) return fail(RT_E_ARG, "perm is NULL or misaligned");
+  const size_t esize = s->dtype == RT_BF16 ? 2 : 4;
+  const size_t bytes = (size_t)s->B * s->H * s->N * s->d_pad * esize;
+  const char* a0 = (const char*)src;
+  const char* b0 = (const char*)dst;
+  if (a0 < b0 + bytes && b0 < a0 + bytes) return fail(RT_E_ARG, "src and dst overlap (the reorder is not in place)");
+  if ((st = check_device()) != RT_OK) return st;
+  rettn::PermuteArgs a{};
+  a.src = src;
+  a.dst = dst;
+  a.perm = perm;
+  a.BH = s->B * s->H;
+  a.N = s->N;
+  a.cpr = (int32_t)(s->d_pad * esize / 16);
+  a.inverse = inverse;
+  hipStream_t hs = (hipStream_t)stream;
+  return launched(rettn::launch_permute(a, hs), hs, "rt_permute_rows");
+}
+
 }  // extern "C"

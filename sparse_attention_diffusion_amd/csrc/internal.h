@@ -50,6 +50,20 @@ struct XcdGrid {
 };
 inline XcdGrid make_xcd_grid(uint32_t total) { return XcdGrid{total, (total + 7u) / 8u}; }
 
+struct PermuteArgs {
+  const void* src;
+  void* dst;
+  const int32_t* perm;     // [N], device
+  int32_t BH, N;
+  int32_t cpr;             // 16-byte chunks per row
+  int32_t inverse;         // 0: dst[i] = src[perm[i]]; 1: dst[perm[i]] = src[i]
+};
+
+// Host: Hilbert-curve order of a grid (text tokens first).  perm has
+// n_text + prod(dims) entries.
+void hilbert_order(const int32_t* dims, int ndims, int n_text, int32_t* perm);
+
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 hipError_t launch_attn_bf16(AttnMode mode, int D, const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(AttnMode mode, int D, const AttnArgs& a, hipStream_t s);
 hipError_t launch_select(bool bf16, int D, const SelectArgs& a, hipStream_t s);

@@ -61,6 +61,8 @@ def _load():
         "rt_step_workspace_bytes": (SZ, [S]),
         "rt_attention_step": (I32, [S, P, P, P, ctypes.POINTER(I32), I32, P, I32, I32, I32, P, P, SZ, P,
                                     ctypes.POINTER(I32)]),
+        "rt_hilbert_order": (I32, [ctypes.POINTER(I32), I32, I32, ctypes.POINTER(I32), I32]),
+        "rt_permute_rows": (I32, [S, P, P, P, I32, P]),
         "rt_attention_step_ex": (I32, [S, P, P, P, ctypes.POINTER(I32), I32, P, I32, I32, I32, I32, I32, P, P, SZ,
                                        P, ctypes.POINTER(I32)]),
     }
@@ -78,7 +80,7 @@ SYMBOLS = [
     "rt_stats_cache_init_ex", "rt_stats_cache_view",
     "rt_stats_cache_set_valid", "rt_stats_cache_invalidate", "rt_stats_cache_destroy", "rt_calibrate",
     "rt_sparse_attn_reshape", "rt_sparse_attn_reshape_ex", "rt_schedule_is_calibration", "rt_step_workspace_bytes", "rt_attention_step",
-    "rt_attention_step_ex",
+    "rt_attention_step_ex", "rt_hilbert_order", "rt_permute_rows",
 ]
 
 
@@ -264,3 +266,19 @@ def rt_attention_step_ex(sh, q, k, v, forced, cache, layer, step, period, varian
                                      0 if workspace is None else workspace.numel() * workspace.element_size(),
                                      _stream(stream), ctypes.byref(did)))
     return bool(did.value)
+
+
+def rt_hilbert_order(dims, n_text=0):
+    """Hilbert-curve token order (host): numpy int32 permutation, text first."""
+    import numpy as np
+    d = (ctypes.c_int32 * len(dims))(*[int(x) for x in dims])
+    n = int(n_text) + int(np.prod([int(x) for x in dims]))
+    out = np.empty(n, dtype=np.int32)
+    _check(_lib.rt_hilbert_order(d, len(dims), int(n_text), out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n))
+    return out
+
+
+def rt_permute_rows(sh, src, dst, perm, inverse=False, stream=None):
+    """Row reorder on the device: dst[..., i, :] = src[..., perm[i], :] (or the inverse)."""
+    _check(_lib.rt_permute_rows(ctypes.byref(sh), _ptr(src), _ptr(dst), _ptr(perm), 1 if inverse else 0,
+                                _stream(stream)))

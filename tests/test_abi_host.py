@@ -4,6 +4,7 @@ import os
 import re
 
 import pytest
+import numpy as np
 import torch
 
 from sparse_attention_diffusion_amd import rettn
@@ -239,3 +240,40 @@ def test_no_device_is_reported_not_faked():
     p = ctypes.c_void_p(4096)
     st = lib.rt_select_blocks(ctypes.byref(sh), p, p, None, 0, p, None, p, 1 << 20, None)
     assert st == rettn.RT_E_DEVICE
+
+
+@pytest.mark.parametrize("dims,n_text", [((2, 2), 0), ((16, 16), 0), ((32, 32), 0), ((64, 64), 0), ((3, 5, 6), 7),
+                                         ((13, 30, 45), 226), ((7,), 3), ((1, 1, 1), 0), ((5, 64), 1)])
+def test_hilbert_order_matches_oracle(dims, n_text):
+    """The library's host Hilbert order is the oracle's, element for element."""
+    import oracle.hilbert
+    got = rettn.rt_hilbert_order(dims, n_text)
+    assert np.array_equal(got, oracle.hilbert.token_order(dims, n_text))
+
+
+def test_hilbert_order_errors():
+    lib = rettn.lib()
+    out = (ctypes.c_int32 * 64)()
+    dims = (ctypes.c_int32 * 4)(4, 4, 4, 4)
+    assert lib.rt_hilbert_order(dims, 0, 0, out, 1) == rettn.RT_E_ARG
+    assert lib.rt_hilbert_order(dims, 4, 0, out, 256) == rettn.RT_E_ARG
+    assert lib.rt_hilbert_order(dims, 2, 0, out, 15) == rettn.RT_E_ARG   # n != n_text + 16
+    assert lib.rt_hilbert_order(dims, 2, -1, out, 15) == rettn.RT_E_ARG
+    bad = (ctypes.c_int32 * 2)(4, 0)
+    assert lib.rt_hilbert_order(bad, 2, 0, out, 0) == rettn.RT_E_ARG
+    big = (ctypes.c_int32 * 2)(300, 300)
+    assert lib.rt_hilbert_order(big, 2, 0, out, 90000) == rettn.RT_E_SHAPE
+    assert lib.rt_hilbert_order(None, 2, 0, out, 16) == rettn.RT_E_ARG
+
+
+def test_permute_rows_argument_errors():
+    lib = rettn.lib()
+    sh = rettn.shape(1, 1, 128, 64, 64, 1)
+    p = ctypes.c_void_p(4096)
+    q = ctypes.c_void_p(4096 + 128 * 64 * 2)
+    assert lib.rt_permute_rows(ctypes.byref(sh), p, q, p, 2, None) == rettn.RT_E_ARG   # inverse flag
+    assert lib.rt_permute_rows(ctypes.byref(sh), p, p, p, 0, None) == rettn.RT_E_ARG   # in place
+    assert lib.rt_permute_rows(ctypes.byref(sh), p, ctypes.c_void_p(4096 + 64), p, 0, None) == rettn.RT_E_ARG
+    assert lib.rt_permute_rows(ctypes.byref(sh), p, q, None, 0, None) == rettn.RT_E_ARG
+    if not torch.cuda.is_available():
+        assert lib.rt_permute_rows(ctypes.byref(sh), p, q, p, 0, None) == rettn.RT_E_DEVICE

@@ -589,3 +589,88 @@ def test_cogvideox5b_layers_and_recalibration():
     views = [cache.tensors(layer) for layer in (0, 1, cfg["layers"] - 1)]
     assert views[0]["valid"] == 1 and views[1]["valid"] == 0 and views[2]["valid"] == 1
     assert not torch.equal(views[0]["m"], views[2]["m"])
+
+
+# ------------------------------------------------------------------ token order (Hilbert)
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 80), ("f32", 64), ("f32", 80)])
+def test_permute_rows_bit_exact(dtype, D):
+    """rt_permute_rows gathers and scatters whole rows exactly like the oracle's
+    fancy indexing, for the Hilbert order and for a random permutation; the
+    inverse undoes the gather."""
+    import oracle.hilbert as oh
+    say("permute rows", dtype, D)
+    B, H, N = 2, 3, 13 * 30 * 45 // 5 + 7
+    x = synth.random_qkv(B, H, N, D, D, seed=D, scale=1.0, dtype=dtype, device=gu.DEV)[0]
+    sh = rettn.shape(B, H, N, D, D, 1, dtype)
+    rng = np.random.default_rng(D)
+    for perm in (rettn.rt_hilbert_order((13, 6, 45), 7), rng.permutation(N).astype(np.int32)):
+        pd = torch.as_tensor(perm).to(gu.DEV)
+        y, z = torch.empty_like(x), torch.empty_like(x)
+        rettn.rt_permute_rows(sh, x, y, pd)
+        rettn.rt_permute_rows(sh, y, z, pd, inverse=True)
+        torch.cuda.synchronize()
+        raw = x.cpu().view(torch.int16 if dtype == "bf16" else torch.float32).numpy()  # bit patterns
+        ref = torch.as_tensor(oh.permute_rows(raw, perm)).view(x.dtype)
+        assert torch.equal(y.cpu(), ref)
+        assert torch.equal(z, x)
+
+
+@pytest.mark.parametrize("name", ["pixart1024", "cogvideox2b"])
+def test_hilbert_ordered_layer(name):
+    """A layer in Hilbert token order: Q, K, V reordered on the device, lists,
+    calibration and a later sparse step in that order, output put back; the
+    oracle does the same with its own order and reorder.  cogvideox2b is
+    checked on sampled query blocks of two heads."""
+    import oracle.hilbert as oh
+    say("hilbert ordered layer", name)
+    cfg = configs.CONFIGS[name] if name == "pixart1024" else small_cfg(name, H=2)
+    sh = rettn.shape_of(cfg)
+    N, d, keep = cfg["N"], cfg["d"], cfg["keep"]
+    forced = configs.forced_blocks(cfg)
+    perm = rettn.rt_hilbert_order(cfg["grid"][1:], cfg["n_text"])
+    assert np.array_equal(perm, oh.token_order(cfg["grid"][1:], cfg["n_text"]))
+    pd = torch.as_tensor(perm).to(gu.DEV)
+    (q0, k0, v0), (q1, k1, v1) = gu.gpu_inputs(cfg, 2, seed=23)
+
+    def reorder(t):
+        out = torch.empty_like(t)
+        rettn.rt_permute_rows(sh, t, out, pd)
+        return out
+    pq0, pk0, pv0, pq1, pk1, pv1 = (reorder(t) for t in (q0, k0, v0, q1, k1, v1))
+    gpu_idx, _ = gu.select(sh, pq0, pk0, forced)
+    # oracle: its own reorder of the stored inputs, then the method, then back
+    hq0, hk0, hv0, hq1, hk1, hv1 = (oh.permute_rows(gu.host(t), perm) for t in (q0, k0, v0, q1, k1, v1))
+    ref_scores = oracle.pooled_scores(hq0, hk0, N, d)
+    ref_idx = oracle.select_blocks(None, None, N, d, keep, forced, scores=ref_scores)
+    gi = gpu_idx.cpu().numpy()
+    for b, h, i in zip(*np.nonzero((gi != ref_idx).any(axis=-1))):  # disagreements only at near-ties
+        a, r = set(gi[b, h, i]), set(ref_idx[b, h, i])
+        tau = min(ref_scores[b, h, i, j] for j in r if j not in forced)
+        assert all(abs(ref_scores[b, h, i, j] - tau) < 1e-5 for j in a ^ r), (b, h, i)
+    idx = torch.as_tensor(ref_idx).to(gu.DEV)
+    cache = rettn.StatsCache(sh, 1)
+    pcal = gu.calibrate(sh, pq0, pk0, pv0, idx, cache)
+    psp = gu.sparse(sh, pq1, pk1, pv1, cache)
+    o_cal, o_sp = torch.empty_like(pcal), torch.empty_like(psp)
+    rettn.rt_permute_rows(sh, pcal, o_cal, pd, inverse=True)
+    rettn.rt_permute_rows(sh, psp, o_sp, pd, inverse=True)
+    torch.cuda.synchronize()
+    if name == "pixart1024":
+        ref_cal = oracle.calibrate(hq0, hk0, hv0, ref_idx, N, d)
+        gu.assert_close(gu.host(o_cal), oh.permute_rows(ref_cal["o"], perm, inverse=True), what="calibrate")
+        ref = oracle.sparse_reshape(hq1, hk1, hv1, ref_idx, ref_cal, N, d)
+        gu.assert_close(gu.host(o_sp), oh.permute_rows(ref, perm, inverse=True), what="sparse")
+    else:
+        nb = configs.n_blocks(N)
+        pos = np.empty_like(perm)
+        pos[perm] = np.arange(N)  # position of each original token in the new order
+        for b, h in ((0, 0), (1, 1)):
+            for i in gu.sample_blocks(nb):
+                rows = gu.block_rows(N, i)  # rows of the reordered sequence
+                st = oracle.calibrate_rows(hq0[b, h], hk0[b, h], hv0[b, h], rows, ref_idx[b, h, i], N, d)
+                orig = perm[rows]
+                gu.assert_close(gu.host(o_cal[b, h, orig]), st["o"], what=f"cal b{b} h{h} blk{i}")
+                ro = oracle.sparse_reshape_rows(hq1[b, h], hk1[b, h], hv1[b, h], rows, ref_idx[b, h, i], st["m"],
+                                                st["z_full"], st["z_sparse"], st["r"], N, d)
+                gu.assert_close(gu.host(o_sp[b, h, orig]), ro, what=f"sparse b{b} h{h} blk{i}")
+    cache.close()
