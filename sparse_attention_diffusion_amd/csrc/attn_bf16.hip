@@ -241,6 +241,36 @@ __device__ __forceinline__ void k_half(u32x4 (&a)[KS], const uint32_t (&ad)[KS],
   }
 }
 
+// K operands of one 32-key half at the immediate LDS offset OFF: KS
+// ds_read_b128 waited for in the same statement.
+template <int KS, int OFF>
+__device__ __forceinline__ void k_half_at(u32x4 (&a)[KS], const uint32_t (&ad)[KS]) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  if constexpr (KS == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:%8\n\t"
+        "ds_read_b128 %1, %5 offset:%8\n\t"
+        "ds_read_b128 %2, %6 offset:%8\n\t"
+        "ds_read_b128 %3, %7 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "i"(OFF)
+        : "memory");
+  } else {
+    static_assert(KS == 5, "k-steps");
+    asm volatile(
+        "ds_read_b128 %0, %5 offset:%10\n\t"
+        "ds_read_b128 %1, %6 offset:%10\n\t"
+        "ds_read_b128 %2, %7 offset:%10\n\t"
+        "ds_read_b128 %3, %8 offset:%10\n\t"
+        "ds_read_b128 %4, %9 offset:%10\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "i"(OFF)
+        : "memory");
+  }
+}
+
 // V^T operands of one d tile for the four k-steps (t, hs): eight
 // ds_read_b64_tr_b16, waited for in the same statement.  h[t][hs][hh].
 template <int OFF, int T, int HS>
@@ -397,6 +427,57 @@ __device__ __forceinline__ void pv(f32x16 (&o)[Shape<D>::NT], const bf16x8 (&p)[
   u32x2 h[Shape<D>::NT][2][2][2];
   v_fetch<D, SLOT_OFF>(h, fr);
   pv_mfma<D>(o, p, h);
+}
+
+// The same two products with fewer operand registers live at once (K one
+// 32-key half at a time, V^T one d tile at a time), for head dims whose
+// accumulators leave little register room.
+template <int D, int SLOT_OFF>
+__device__ __forceinline__ void scores_lean(f32x16 (&s)[2], const Rows<D>& st, const Frag<D>& fr, int nvalid) {
+  constexpr int KS = Shape<D>::KS;
+  {
+    u32x4 kk[KS];
+    k_half_at<KS, SLOT_OFF>(kk, fr.k);
+    s[0] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kk[ks]), st.q[ks], s[0], 0, 0, 0);
+  }
+  {
+    u32x4 kk[KS];
+    k_half_at<KS, SLOT_OFF + 32 * Shape<D>::ROW>(kk, fr.k);
+    s[1] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kk[ks]), st.q[ks], s[1], 0, 0, 0);
+  }
+  if (nvalid < kBlock) {
+    const int g = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = 32 * t + (i >> 2) * 8 + 4 * g + (i & 3);
+        if (key >= nvalid) s[t][i] = -INFINITY;
+      }
+  }
+}
+
+template <int D, int SLOT_OFF>
+__device__ __forceinline__ void pv_lean(f32x16 (&o)[Shape<D>::NT], const bf16x8 (&p)[2][2], const Frag<D>& fr) {
+  constexpr int ROW = Shape<D>::ROW;
+#pragma unroll
+  for (int dt = 0; dt < Shape<D>::NT; ++dt) {
+    u32x2 h[2][2][2];
+    tr_reads<SLOT_OFF, 32 * ROW, 16 * ROW>(h, fr.v[dt][0], fr.v[dt][1]);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        const u32x4 both = __builtin_shufflevector(h[t][hs][0], h[t][hs][1], 0, 1, 2, 3);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), p[t][hs], o[dt], 0, 0, 0);
+      }
+  }
 }
 
 // Q^T operand of this lane's row.  Rows >= N read row N-1 instead (every lane
@@ -792,7 +873,8 @@ struct CalibCtx {
     if (!active) return;
     const bool kept = __builtin_amdgcn_readfirstlane(flags[j]) != 0;
     f32x16 s[2];
-    scores<D, SLOT * Shape<D>::SLOT>(s, st, fr, min(kBlock, N - j * kBlock));
+    if constexpr (D == 80) scores_lean<D, SLOT * Shape<D>::SLOT>(s, st, fr, min(kBlock, N - j * kBlock));
+    else scores<D, SLOT * Shape<D>::SLOT>(s, st, fr, min(kBlock, N - j * kBlock));
     bool any;
     const float corr = update_max(st.m_ref, st.m_true, row_max(s), c, &any);
     if (any) {
@@ -808,16 +890,19 @@ struct CalibCtx {
     const float zb = probs(p, s, st.m_ref, c);
     if (kept) {
       zk += zb;
-      pv<D, SLOT * Shape<D>::SLOT>(okept, p, fr);
+      if constexpr (D == 80) pv_lean<D, SLOT * Shape<D>::SLOT>(okept, p, fr);
+      else pv<D, SLOT * Shape<D>::SLOT>(okept, p, fr);
     } else {
       zm += zb;
-      pv<D, SLOT * Shape<D>::SLOT>(ores, p, fr);
+      if constexpr (D == 80) pv_lean<D, SLOT * Shape<D>::SLOT>(ores, p, fr);
+      else pv<D, SLOT * Shape<D>::SLOT>(ores, p, fr);
     }
   }
 };
 
 template <int D, int NBUF, int QB, bool RB>
-__global__ void __launch_bounds__(128 * QB) calib_kernel(AttnArgs a, XcdGrid grid) {
+__global__ void __launch_bounds__(128 * QB) __attribute__((amdgpu_waves_per_eu(D == 80 ? 2 : 1, 4)))
+calib_kernel(AttnArgs a, XcdGrid grid) {
   constexpr int NT = Shape<D>::NT;
   static_assert(NBUF >= 2 && NBUF <= 3, "ring depth");
   __shared__ __attribute__((aligned(1024))) char ring[NBUF * Shape<D>::SLOT];
