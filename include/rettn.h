@@ -3,7 +3,7 @@
  *
  * What it computes.  The Re-ttention project page ("Re-ttention: Ultra Sparse
  * Visual Generation via Attention Statistical Reshape") describes attention for
- * diffusion transformers that keeps only a small subset of the keys (Abstract:
+ * diffusion transformers that keeps few of the keys (Abstract:
  * down to 3.1% of the tokens) and corrects the resulting softmax
  * normalisation shift with statistics cached at an earlier denoising step
  * (teaser paragraph), namely the ratio of sparse to full softmax denominators

@@ -1,7 +1,7 @@
 // Block selector: mean-pooled Q/K per 64-token block, pooled logits, and a
 // per-query-block top-k with always-kept (forced) blocks.
 //
-// Method: the Re-ttention project page keeps only a small subset of the tokens
+// Method: the Re-ttention project page keeps just a few of the tokens
 // (Abstract: as few as 3.1%).  How the subset is chosen is not spelled out
 // there; this library scores 64-token blocks by the scaled dot product of
 // their mean query and mean key and keeps, per query block, the forced blocks
