@@ -33,6 +33,7 @@ SHORT = [("sparse_occ_kernel<64, false, false>", "sparse reshape R1 (d_pad 64)")
          ("sparse_occ_kernel<80, false, true>", "sparse reshape R2 (d_pad 80)"),
          ("sparse_occ_kernel<80, true, true>", "sparse reshape R2, bf16 residual (d_pad 80)"),
          ("calib_kernel<64, 2, 2, true>", "calibration, bf16 residual (d_pad 64)"),
+         ("calib_kernel<80, 2, 2, true>", "calibration, bf16 residual (d_pad 80)"),
          ("calib_kernel<64", "calibration (d_pad 64)"), ("calib_kernel<80", "calibration (d_pad 80)"),
          ("attn_f32_kernel", "float32 attention"), ("select_kernel", "block top-k"), ("pool_kernel", "block pooling")]
 
