@@ -49,6 +49,8 @@ def block_constant_inputs(B, H, N, D, seed, dtype):
 @pytest.mark.parametrize("N,keep,forced,dtype", [
     (1000, 5, [0, 7], "bf16"), (256, 2, [], "f32"), (64 * 37 + 5, 9, [0, 1, 2, 3], "bf16"),
     (65536, 9, [0, 1, 2, 3], "bf16"), (640, 10, [], "bf16"), (130, 1, [2], "bf16"),
+    # more than 32 non-forced winners: the bitonic-sort path (and every block kept in the second case)
+    (64 * 100, 45, [3], "bf16"), (64 * 40, 40, [0], "bf16"), (64 * 600 + 17, 40, [], "bf16"),
 ])
 def test_selector_exact_on_exact_scores(N, keep, forced, dtype):
     say("selector exact", N, keep, forced, dtype)
