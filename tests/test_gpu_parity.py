@@ -407,6 +407,37 @@ def test_edge_shapes(N, d, D, keep, forced, dtype, variant):
     assert np.array_equal(idx.cpu().numpy(), ref_idx)
 
 
+@pytest.mark.parametrize("keep", [9, 1024])
+def test_maximum_sequence_length(keep):
+    """N = 65536 (1024 key blocks, the largest supported), with a few kept
+    blocks and with every block kept: selector lists against the oracle's on
+    exactly representable scores is covered elsewhere; here the oracle's lists
+    drive calibration and a later sparse step, checked on sampled query blocks
+    (first, middle, last)."""
+    say("maximum N", keep)
+    B, H, N, d = 1, 1, 65536, 64
+    nb = N // 64
+    forced = [0]
+    (q0, k0, v0), (q1, k1, v1) = (synth.random_qkv(B, H, N, d, d, seed=s, scale=1.0, dtype="bf16", device=gu.DEV)
+                                  for s in (41, 42))
+    sh = rettn.shape(B, H, N, d, d, keep, "bf16")
+    ref_idx = oracle.select_blocks(gu.host(q0), gu.host(k0), N, d, keep, forced)
+    cache = rettn.StatsCache(sh, 1)
+    o_cal = gu.calibrate(sh, q0, k0, v0, torch.as_tensor(ref_idx).to(gu.DEV), cache)
+    o = gu.sparse(sh, q1, k1, v1, cache)
+    torch.cuda.synchronize()
+    qh0, kh0, vh0 = (gu.host(x[0, 0]) for x in (q0, k0, v0))
+    qh1, kh1, vh1 = (gu.host(x[0, 0]) for x in (q1, k1, v1))
+    for i in (0, nb // 2, nb - 1):
+        rows = gu.block_rows(N, i)
+        st = oracle.calibrate_rows(qh0, kh0, vh0, rows, ref_idx[0, 0, i], N, d)
+        gu.assert_close(gu.host(o_cal[0, 0, rows]), st["o"], what=f"calibrate blk{i}")
+        ro = oracle.sparse_reshape_rows(qh1, kh1, vh1, rows, ref_idx[0, 0, i], st["m"], st["z_full"],
+                                        st["z_sparse"], st["r"], N, d)
+        gu.assert_close(gu.host(o[0, 0, rows]), ro, what=f"sparse blk{i}")
+    cache.close()
+
+
 @pytest.mark.parametrize("keep,variant", [(1, "r1"), (2, "r1"), (3, "r1"), (9, "r1"), (1, "r2"), (9, "r2")])
 def test_sparse_many_blocks_per_workgroup(keep, variant):
     """The sparse kernel where each persistent workgroup walks several query
