@@ -22,3 +22,17 @@ def test_header_is_c_and_host_calls_work(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip() == "ok"
+
+
+@pytest.mark.gpu
+def test_c_program_drives_the_gpu_path():
+    """tests/c_gpu_check.c (built by __graft_entry__.build()): selector, calibration,
+    R1 and R2 sparse steps and the token reorder driven from C with HIP runtime
+    memory only; the sparse steps reproduce the calibration output on its own
+    inputs and the reorder round-trips bit for bit."""
+    exe = os.path.join(ROOT, "tests", "_bin", "c_gpu_check")
+    assert os.path.exists(exe), "build() has not been run"
+    print("c_gpu_check", flush=True)
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert out.stdout.strip() == "ok"
