@@ -1,0 +1,80 @@
+"""Host logic of the measurement code (no GPU): the benchmark's FLOP and byte
+counts, its command-line contract, and the rocprofv3 summariser."""
+import csv
+import importlib.util
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+from sparse_attention_diffusion_amd import profsum
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_module", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_kept_flops_and_bytes_by_hand():
+    bench = _bench()
+    # one head, N = 150 (blocks of 64, 64, 22), keep 2
+    idx = np.array([[[[0, 2], [1, 2], [0, 1]]]], dtype=np.int32)
+    d, D, N = 64, 64, 150
+    # rows x kept keys per query block: 64*(64+22) + 64*(64+22) + 22*(64+64)
+    assert bench.kept_flops(idx, N, d) == 4 * d * (64 * 86 + 64 * 86 + 22 * 128)
+    # Q, O (bf16), R (f32), m/Z_full/Z_sparse (f32) per row, K and V of blocks {0,1,2} once, the lists
+    rows = N
+    want = rows * D * 2 * 2 + rows * D * 4 + rows * 12 + 150 * D * 2 * 2 + idx.size * 4
+    assert bench.sparse_call_bytes(idx, N, D, 2) == want
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+def _write_csv(path, header, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_profile_summary_from_csv(tmp_path):
+    trace = tmp_path / "trace"
+    trace.mkdir()
+    _write_csv(trace / "run_kernel_stats.csv", ["Name", "Calls", "TotalDurationNs", "AverageNs", "MinNs", "MaxNs"], [
+        ["void rettn::(anonymous namespace)::sparse_occ_kernel<64, false, false>(rettn::AttnArgs)", 10, 3e6, 3e5,
+         2.9e5, 3.1e5],
+        ["void rettn::(anonymous namespace)::calib_kernel<64, 2, 2, false>(rettn::AttnArgs)", 1, 6e6, 6e6, 6e6, 6e6],
+        ["some_other_kernel", 3, 1e3, 3e2, 2e2, 4e2],
+    ])
+    stats = {s["kernel"]: s for s in profsum.trace_stats(str(trace))}
+    assert set(stats) == {"sparse reshape R1 (d_pad 64)", "calibration (d_pad 64)"}
+    assert stats["sparse reshape R1 (d_pad 64)"]["avg_us"] == 300.0
+    assert stats["calibration (d_pad 64)"]["total_ms"] == 6.0
+    # counters: a 512 MiB copy read back as 262144 KiB means a fetch scale of 2
+    pmc = tmp_path / "pmc"
+    pmc.mkdir()
+    _write_csv(pmc / "run_counter_collection.csv", ["Kernel_Name", "Counter_Name", "Counter_Value"], [
+        ["copyBuffer", "FETCH_SIZE", 262144.0],
+        ["sparse_occ_kernel<64, false, false>", "FETCH_SIZE", 500000.0],
+        ["sparse_occ_kernel<64, false, false>", "FETCH_SIZE", 700000.0],
+    ])
+    scale, per, raw = profsum.counters(str(pmc), "FETCH_SIZE")
+    assert raw == 262144.0 and abs(scale - 2.0) < 1e-12
+    assert abs(per["sparse reshape R1 (d_pad 64)"] - 600000.0 * 1024 * 2) < 1e-3
+    # every kernel of the library has a label, and the bf16/R2 variants are not merged with R1
+    names = ["sparse_occ_kernel<64, true, false>", "sparse_occ_kernel<64, false, true>",
+             "sparse_occ_kernel<80, true, true>", "calib_kernel<80, 2, 2, true>", "pool_kernel<__bf16, 64>",
+             "select_kernel<64, 5>", "attn_f32_kernel<64, 1>"]
+    labels = [profsum.short_name(n) for n in names]
+    assert None not in labels and len(set(labels)) == len(labels)
