@@ -85,9 +85,67 @@ def counters(d, counter):
     return scale, {k: sum(v) / len(v) * 1024.0 * scale for k, v in per.items()}, max(copy)
 
 
+XCDS, CUS, SIMDS = 8, 256, 1024
+
+# counter passes of the unit-utilisation summary (each fits one rocprofv3 --pmc run)
+UNIT_PASSES = [
+    "GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_COEXEC_CYCLES",
+    "GRBM_GUI_ACTIVE TA_TA_BUSY_sum TD_TD_BUSY_sum TCP_TCC_READ_REQ_sum TCP_TCC_READ_REQ_LATENCY_sum "
+    "TCP_PENDING_STALL_CYCLES_sum",
+]
+
+
+def unit_counters(dirs):
+    """Mean per dispatch of every counter, per labelled kernel, with the GRBM
+    cycle count of the same pass (counters of one pass are ratios of it)."""
+    per = {}
+    for d in dirs:
+        rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*counter_collection.csv")))))
+        acc = {}
+        for r in rows:
+            label = short_name(r["Kernel_Name"])
+            if label:
+                acc.setdefault(label, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        for label, cs in acc.items():
+            if "GRBM_GUI_ACTIVE" not in cs:
+                raise RuntimeError(f"{d}: every pass needs GRBM_GUI_ACTIVE")
+            grbm = sum(cs["GRBM_GUI_ACTIVE"]) / len(cs["GRBM_GUI_ACTIVE"])
+            for name, v in cs.items():
+                if name != "GRBM_GUI_ACTIVE":
+                    per.setdefault(label, {})[name] = (sum(v) / len(v), grbm)
+    return per
+
+
+def unit_table(per):
+    """Utilisation per kernel.  GRBM_GUI_ACTIVE is summed over the XCDs, so one
+    XCD's cycles are GRBM / 8; SQ wave counters count 4-cycle units."""
+    lines = ["| kernel | MFMA busy | VALU active | MFMA+VALU co-issue | TA busy | TD busy | L1 pending-stall | "
+             "L1→L2 reads | mean latency (cycles) | reads in flight per CU |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for label in sorted(per):
+        c = per[label]
+
+        def frac(name, units, scale=1.0):
+            if name not in c:
+                return None
+            v, grbm = c[name]
+            return v * scale / (grbm / XCDS * units)
+        req = c.get("TCP_TCC_READ_REQ_sum")
+        lat = c.get("TCP_TCC_READ_REQ_LATENCY_sum")
+        cells = [frac("SQ_VALU_MFMA_BUSY_CYCLES", SIMDS), frac("SQ_ACTIVE_INST_VALU", SIMDS, 4.0),
+                 frac("SQ_VALU_MFMA_COEXEC_CYCLES", SIMDS), frac("TA_TA_BUSY_sum", CUS), frac("TD_TD_BUSY_sum", CUS),
+                 frac("TCP_PENDING_STALL_CYCLES_sum", CUS)]
+        txt = ["–" if x is None else f"{100 * x:.0f}%" for x in cells]
+        txt.append("–" if req is None else f"{req[0] / 1e6:.1f} M")
+        txt.append("–" if not (req and lat) else f"{lat[0] / req[0]:.0f}")
+        txt.append("–" if lat is None else f"{lat[0] / (lat[1] / XCDS * CUS):.0f}")
+        lines.append(f"| {label} | " + " | ".join(txt) + " |")
+    return lines
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--trace", required=True)
+    ap.add_argument("--trace")
+    ap.add_argument("--units", nargs="+", help="counter directories of the UNIT_PASSES runs")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--config", default="cogvideox2b")
@@ -96,6 +154,17 @@ def main():
     ap.add_argument("--out", required=True)
     args = ap.parse_args()
     os.makedirs(args.out, exist_ok=True)
+    if args.units:
+        lines = [f"# Unit utilisation per kernel (rocprofv3 --pmc): {args.config}", "", "Commands (one run per pass):",
+                 ""] + ["    " + args.command.replace("COUNTERS", p) for p in UNIT_PASSES] + [
+                 "", "Fractions are of the kernel's own active cycles (GRBM_GUI_ACTIVE per XCD) over all 1024 "
+                 "SIMDs or 256 CUs.", ""] + unit_table(unit_counters(args.units)) + [
+                 "", f"Kernel source sha256[:16] of attn_bf16.hip: {source_hash()}"]
+        open(os.path.join(args.out, f"units_{args.config}.md"), "w").write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        return
+    if not args.trace:
+        ap.error("--trace is required")
     stats = trace_stats(args.trace)
     lines = [f"# rocprofv3 kernel trace: {args.config}", "", "Command:", "", "    " + args.command, "",
              "| kernel | calls | avg us | min us | max us | total ms |", "|---|---|---|---|---|---|"]

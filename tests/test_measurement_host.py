@@ -78,3 +78,24 @@ def test_profile_summary_from_csv(tmp_path):
              "select_kernel<64, 5>", "attn_f32_kernel<64, 1>"]
     labels = [profsum.short_name(n) for n in names]
     assert None not in labels and len(set(labels)) == len(labels)
+
+
+def test_unit_utilisation_summary(tmp_path):
+    """GRBM_GUI_ACTIVE is summed over 8 XCDs: 8000 cycles means 1000 per XCD, so
+    512000 MFMA-busy cycles over 1024 SIMDs is 50%, and 64000 TA-busy cycles over
+    256 CUs is 25%; a read latency sum of 2560000 cycles over 1000 cycles and 256
+    CUs is 10 reads in flight per CU."""
+    d1, d2 = tmp_path / "u1", tmp_path / "u2"
+    d1.mkdir()
+    d2.mkdir()
+    k = "sparse_occ_kernel<64, false, false>"
+    _write_csv(d1 / "run_counter_collection.csv", ["Kernel_Name", "Counter_Name", "Counter_Value"], [
+        [k, "GRBM_GUI_ACTIVE", 8000], [k, "SQ_VALU_MFMA_BUSY_CYCLES", 512000], [k, "SQ_ACTIVE_INST_VALU", 64000],
+        [k, "SQ_VALU_MFMA_COEXEC_CYCLES", 102400]])
+    _write_csv(d2 / "run_counter_collection.csv", ["Kernel_Name", "Counter_Name", "Counter_Value"], [
+        [k, "GRBM_GUI_ACTIVE", 8000], [k, "TA_TA_BUSY_sum", 64000], [k, "TD_TD_BUSY_sum", 128000],
+        [k, "TCP_TCC_READ_REQ_sum", 5000], [k, "TCP_TCC_READ_REQ_LATENCY_sum", 2560000],
+        [k, "TCP_PENDING_STALL_CYCLES_sum", 25600]])
+    rows = profsum.unit_table(profsum.unit_counters([str(d1), str(d2)]))
+    cells = [x.strip() for x in rows[-1].split("|")[1:-1]]
+    assert cells == ["sparse reshape R1 (d_pad 64)", "50%", "25%", "10%", "25%", "50%", "10%", "0.0 M", "512", "10"]
