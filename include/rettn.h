@@ -49,6 +49,19 @@
  *    their pointers may be NULL.
  *  - Limits: block == 64, d_pad in {64, 80}, 1 <= d <= d_pad,
  *    1 <= keep <= Nb = ceil(N/64), N <= 65536, 0 <= n_forced <= keep.
+ *  - Kept lists (block_idx, and the copy in the cache) hold `keep` int32 block
+ *    indices per query block.  rt_select_blocks writes every row strictly
+ *    ascending.  A caller's row must be non-decreasing; every call reads a
+ *    row as the set of its entries (an entry equal to its predecessor adds
+ *    nothing), so a row with k distinct blocks keeps exactly those k blocks.
+ *    Entries outside [0, Nb) are clamped into range.  A row that is not
+ *    non-decreasing is outside this contract: its results are unspecified,
+ *    but every memory access stays inside the buffers described here.
+ *  - Outputs must not overlap inputs or each other (RT_E_ARG): o must be
+ *    disjoint from q, k, v, the list it reads and the cache layer; the
+ *    selector's block_idx, pooled_scores and workspace from q, k and from one
+ *    another.  The one allowed sharing: rt_calibrate may read its list from
+ *    the layer's own list copy (to recalibrate with the cached lists).
  *  - Calls on the same cache layer must not overlap in time from several
  *    host threads; calls on different layers may.
  */
@@ -91,7 +104,10 @@ typedef struct rt_stats_cache rt_stats_cache;
  *   m, z_full, z_sparse : float32 [B, H, N]
  *   R                   : [B, H, N, d_pad], row-major; float32 by default, bf16
  *                         (reinterpret the pointer) when r_dtype == RT_BF16
- *   idx                 : int32   [B, H, Nb, keep], each row ascending
+ *   idx                 : int32   [B, H, Nb, keep], the kept list used at calibration
+ * (Differs from a plain pointer struct in two fields: `rows` = B*H*N gives the
+ * extent of the row-wise arrays, and `r_dtype` says how R is stored; the row
+ * stride of R is always d_pad elements.)
  * `valid` is 1 once the layer has been calibrated (or marked valid).       */
 typedef struct {
   float* m;

@@ -153,6 +153,35 @@ rt_status check_tensors(const void* const* ptrs, const char* const* names, int n
   return RT_OK;
 }
 
+// A device byte range [p, p + bytes).
+struct Span {
+  const void* p;
+  size_t bytes;
+  const char* name;
+};
+
+bool overlap(const Span& a, const Span& b) {
+  if (a.p == nullptr || b.p == nullptr || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a.p), y = reinterpret_cast<uintptr_t>(b.p);
+  return x < y + b.bytes && y < x + a.bytes;
+}
+
+// Every output span must be disjoint from every input span and from the other
+// outputs (the kernels read inputs while other workgroups write outputs).
+rt_status check_disjoint(const Span* outs, int n_out, const Span* ins, int n_in) {
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlap(outs[i], ins[j])) return fail(RT_E_ARG, "%s overlaps %s", outs[i].name, ins[j].name);
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(outs[i], outs[j])) return fail(RT_E_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+  return RT_OK;
+}
+
+size_t tensor_bytes(const rt_shape* s) { return (size_t)s->B * s->H * s->N * s->d_pad * elem_bytes(s); }
+
+size_t list_bytes(const rt_shape* s) { return (size_t)s->B * s->H * nblocks(s->N) * s->keep * 4; }
+
 rt_status check_cache(const rt_shape* s, const rt_stats_cache* c, int32_t layer) {
   if (c == nullptr) return fail(RT_E_ARG, "cache is NULL");
   if (layer < 0 || layer >= c->n_layers) return fail(RT_E_ARG, "layer %d out of range [0, %d)", layer, c->n_layers);
@@ -210,6 +239,13 @@ rt_status rt_select_blocks(const rt_shape* s, const void* q, const void* k, cons
     return fail(RT_E_ARG, "pooled_scores is not 4-byte aligned");
   if (ws_bytes < select_ws(s)) return fail(RT_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, select_ws(s));
   const int32_t nb = (int32_t)nblocks(s->N);
+  {
+    const Span ins[] = {{q, tensor_bytes(s), "q"}, {k, tensor_bytes(s), "k"}};
+    const Span outs[] = {{block_idx, list_bytes(s), "block_idx"},
+                         {pooled_scores, (size_t)s->B * s->H * nb * nb * 4, "pooled_scores"},
+                         {workspace, select_ws(s), "workspace"}};
+    if ((st = check_disjoint(outs, 3, ins, 2)) != RT_OK) return st;
+  }
   if (n_forced < 0 || n_forced > s->keep) return fail(RT_E_ARG, "need 0 <= n_forced <= keep (n_forced=%d)", n_forced);
   if (n_forced > 0 && forced == nullptr) return fail(RT_E_ARG, "forced is NULL with n_forced=%d", n_forced);
   SelectArgs a{};
@@ -334,6 +370,21 @@ rt_status rt_calibrate(const rt_shape* s, const void* q, const void* k, const vo
   const void* ptrs[] = {q, k, v, block_idx, o};
   const char* names[] = {"q", "k", "v", "block_idx", "o"};
   if ((st = check_tensors(ptrs, names, 5)) != RT_OK) return st;
+  {
+    const Span ins[] = {{q, tensor_bytes(s), "q"}, {k, tensor_bytes(s), "k"}, {v, tensor_bytes(s), "v"}};
+    const Span outs[] = {{o, tensor_bytes(s), "o"},
+                         {c->base + (size_t)layer * c->layer_stride, c->layer_stride, "the cache layer"}};
+    if ((st = check_disjoint(outs, 2, ins, 3)) != RT_OK) return st;
+    const Span lst[] = {{block_idx, list_bytes(s), "block_idx"}};
+    if ((st = check_disjoint(outs, 1, lst, 1)) != RT_OK) return st;  // o vs the list it reads
+    // The list may be the layer's own list copy (each workgroup reads its
+    // entries before writing the same values back), or lie outside the layer.
+    char* layer_base = c->base + (size_t)layer * c->layer_stride;
+    if ((const void*)block_idx != (const void*)(layer_base + c->off_idx)) {
+      const Span lay[] = {{layer_base, c->layer_stride, "the cache layer"}};
+      if ((st = check_disjoint(lst, 1, lay, 1)) != RT_OK) return st;
+    }
+  }
   if ((st = check_device()) != RT_OK) return st;
   AttnArgs a = attn_args(s, q, k, v, o, block_idx, c, layer);
   hipStream_t hs = (hipStream_t)stream;
@@ -364,6 +415,15 @@ rt_status rt_sparse_attn_reshape_ex(const rt_shape* s, const void* q, const void
   const char* names[] = {"q", "k", "v", "o"};
   if ((st = check_tensors(ptrs, names, 4)) != RT_OK) return st;
   if (block_idx != nullptr && !aligned16(block_idx)) return fail(RT_E_ARG, "block_idx is not 16-byte aligned");
+  {
+    const Span ins[] = {{q, tensor_bytes(s), "q"},
+                        {k, tensor_bytes(s), "k"},
+                        {v, tensor_bytes(s), "v"},
+                        {block_idx, list_bytes(s), "block_idx"},
+                        {c->base + (size_t)layer * c->layer_stride, c->layer_stride, "the cache layer"}};
+    const Span outs[] = {{o, tensor_bytes(s), "o"}};
+    if ((st = check_disjoint(outs, 1, ins, 5)) != RT_OK) return st;
+  }
   if ((st = check_device()) != RT_OK) return st;
   AttnArgs a = attn_args(s, q, k, v, o, nullptr, c, layer);
   a.idx = block_idx != nullptr ? block_idx : a.idx_cache;

@@ -736,6 +736,7 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
 
   for (int k = 0; k < n_items; ++k) {
     float mr = V2 ? -INFINITY : st.mc * kLog2e, z = 0.f;
+    int jprev = -1;  // a list entry equal to its predecessor is walked with every key masked
     for (int n = 0; n < keep; ++n) {
       // 1. K_n has landed (the loads issued after it may still be in flight).
       if (n == 0 && k > 0) wait_vmcnt<NST + NLD>();
@@ -743,7 +744,8 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
       else wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
       dma.issue_at(vslot, vtile, tbytes);
-      const int nvalid = tbytes / (D * 2);
+      const int nvalid = j == jprev ? 0 : tbytes / (D * 2);
+      jprev = j;
       // 2. scores and P, one 32-key half at a time.
       f32x16 s[2];
 #pragma unroll

@@ -31,21 +31,29 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnArgs a, XcdGrid 
   const float* vh = (const float*)a.v + head;
   const int32_t* list = a.idx + ((size_t)bh * Nb + qi) * keep;
 
-  const int nseq = MODE == AttnMode::kCalibrate ? Nb : keep;
-  for (int n = lane; n < keep; n += kThreads) seq[n] = min(max(list[n], 0), Nb - 1);
+  // The row is read as a set: blocks are walked from a flag row, kept ones
+  // first (ascending), then (calibration) the masked ones, so a repeated or
+  // unordered entry counts once, as in every other kernel.
+  for (int n = lane; n < Nb; n += kThreads) flags[n] = 0;
+  __syncthreads();
+  for (int n = lane; n < keep; n += kThreads) flags[min(max(list[n], 0), Nb - 1)] = 1;
+  __syncthreads();
+  int nkept = 0;
+  for (int base = 0; base < Nb; base += 64) {
+    const int j = base + lane;
+    const bool f = j < Nb && flags[j];
+    const unsigned long long mk = __ballot(f);
+    if (f) seq[nkept + __popcll(mk & ((1ull << lane) - 1ull))] = j;
+    nkept += __popcll(mk);
+  }
+  int nseq = nkept;
   if (MODE == AttnMode::kCalibrate) {
-    for (int n = lane; n < Nb; n += kThreads) flags[n] = 0;
-    __syncthreads();
-    for (int n = lane; n < keep; n += kThreads) flags[seq[n]] = 1;
-    __syncthreads();
-    int cnt = keep;
     for (int base = 0; base < Nb; base += 64) {
-      int j = base + lane;
-      bool f = j < Nb && !flags[j];
-      unsigned long long mk = __ballot(f);
-      const int pos = cnt + __popcll(mk & ((1ull << lane) - 1ull));
-        if (f && pos < kMaxBlocks) seq[pos] = j;  // bounded even for a list with repeats
-      cnt += __popcll(mk);
+      const int j = base + lane;
+      const bool f = j < Nb && !flags[j];
+      const unsigned long long mk = __ballot(f);
+      if (f) seq[nseq + __popcll(mk & ((1ull << lane) - 1ull))] = j;
+      nseq += __popcll(mk);
     }
     if (a.idx_cache != nullptr) {
       int32_t* dst = a.idx_cache + ((size_t)bh * Nb + qi) * keep;
@@ -77,7 +85,7 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnArgs a, XcdGrid 
       }
     }
     __syncthreads();
-    if (MODE == AttnMode::kCalibrate && n == keep) {
+    if (MODE == AttnMode::kCalibrate && n == nkept) {
 #pragma unroll
       for (int d = 0; d < D; ++d) { ok[d] = o[d]; o[d] = 0.f; }
       m_kept = m;
@@ -108,7 +116,7 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnArgs a, XcdGrid 
   const size_t srow = (size_t)bh * N + row;
   float* orow = (float*)a.o + srow * D;
   if (MODE == AttnMode::kCalibrate) {
-    if (nseq == keep) {
+    if (nseq == nkept) {
 #pragma unroll
       for (int d = 0; d < D; ++d) { ok[d] = o[d]; o[d] = 0.f; }
       m_kept = m;

@@ -259,6 +259,9 @@ __global__ void __launch_bounds__(64) select_kernel(SelectArgs a, XcdGrid grid, 
 #pragma unroll
       for (int c = 0; c < CH; ++c)
         if (c * 64 < P) keys[c * 64 + lane] = kk[c];
+      // P can exceed the CH*64 keys this lane holds (CH = 5 sorts 512 keys):
+      // the rest of the sort buffer is padding and must lose every compare.
+      for (int t = CH * 64 + lane; t < P; t += 64) keys[t] = 0ull;
       __syncthreads();
       for (int k = 2; k <= P; k <<= 1) {
         for (int jx = k >> 1; jx > 0; jx >>= 1) {
@@ -275,7 +278,10 @@ __global__ void __launch_bounds__(64) select_kernel(SelectArgs a, XcdGrid grid, 
           __syncthreads();
         }
       }
-      for (int t = lane; t < rounds; t += 64) flags[0xFFFFFFFFu - (uint32_t)(keys[t] & 0xFFFFFFFFull)] = 1;
+      // rounds <= Nb - n_forced candidates, so the first `rounds` keys are real;
+      // a padding key (0) is still skipped rather than trusted.
+      for (int t = lane; t < rounds; t += 64)
+        if (keys[t] != 0ull) flags[0xFFFFFFFFu - (uint32_t)(keys[t] & 0xFFFFFFFFull)] = 1;
     }
     __syncthreads();
     emit(flags, Nb, a.idx + ((size_t)bh * Nb + i) * keep);

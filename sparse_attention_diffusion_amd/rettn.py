@@ -10,7 +10,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "_lib", "librettn.so")
+# RETTN_LIB names another build of the same C ABI: the CPU tests use it to run
+# the host checks against a sanitizer build whose kernel launches all fail.
+LIB_PATH = os.environ.get("RETTN_LIB") or os.path.join(_HERE, "_lib", "librettn.so")
 
 RT_OK, RT_E_ARG, RT_E_SHAPE, RT_E_DTYPE, RT_E_STATE, RT_E_WORKSPACE, RT_E_LAUNCH, RT_E_DEVICE = range(8)
 RT_BF16, RT_F32 = 0, 1

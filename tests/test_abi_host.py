@@ -76,6 +76,17 @@ def _fake_dev_memory(nbytes):
     return buf, buf.data_ptr() + off
 
 
+def _addrs(n, spacing=1 << 32):
+    """n distinct, far-apart, 256-byte aligned fake device addresses (never
+    dereferenced on the host: validation only does pointer arithmetic)."""
+    return [ctypes.c_void_p((i + 1) * spacing) for i in range(n)]
+
+
+def _passes_validation(st):
+    """Without a GPU a call that passes validation stops at RT_E_DEVICE."""
+    return st == rettn.RT_E_DEVICE if not torch.cuda.is_available() else True
+
+
 def test_cache_layout_views():
     sh = rettn.shape(1, 2, 100, 64, 64, 2, dtype="f32")
     nbytes = rettn.stats_cache_bytes(sh, 3)
@@ -169,19 +180,67 @@ def test_shape_validation(field, value, status):
 def test_select_argument_errors():
     lib = rettn.lib()
     sh = rettn.shape(1, 1, 200, 64, 64, 2)
-    p = ctypes.c_void_p(4096)
+    q, k, ix, ws = _addrs(4)
     need = rettn.select_workspace_bytes(sh)
     assert need == 2 * 4 * 64 * 4
-    assert lib.rt_select_blocks(ctypes.byref(sh), None, p, None, 0, p, None, p, need, None) == rettn.RT_E_ARG
-    assert lib.rt_select_blocks(ctypes.byref(sh), ctypes.c_void_p(4100), p, None, 0, p, None, p, need, None) \
+    assert lib.rt_select_blocks(ctypes.byref(sh), None, k, None, 0, ix, None, ws, need, None) == rettn.RT_E_ARG
+    assert lib.rt_select_blocks(ctypes.byref(sh), ctypes.c_void_p(4100), k, None, 0, ix, None, ws, need, None) \
         == rettn.RT_E_ARG
-    assert lib.rt_select_blocks(ctypes.byref(sh), p, p, None, 0, p, None, p, need - 1, None) == rettn.RT_E_WORKSPACE
+    assert lib.rt_select_blocks(ctypes.byref(sh), q, k, None, 0, ix, None, ws, need - 1, None) == rettn.RT_E_WORKSPACE
     bad = (ctypes.c_int32 * 3)(0, 1, 2)
-    assert lib.rt_select_blocks(ctypes.byref(sh), p, p, bad, 3, p, None, p, need, None) == rettn.RT_E_ARG
+    assert lib.rt_select_blocks(ctypes.byref(sh), q, k, bad, 3, ix, None, ws, need, None) == rettn.RT_E_ARG
+    assert b"n_forced" in lib.rt_last_error()
     dup = (ctypes.c_int32 * 2)(1, 1)
-    assert lib.rt_select_blocks(ctypes.byref(sh), p, p, dup, 2, p, None, p, need, None) == rettn.RT_E_ARG
+    assert lib.rt_select_blocks(ctypes.byref(sh), q, k, dup, 2, ix, None, ws, need, None) == rettn.RT_E_ARG
+    assert b"twice" in lib.rt_last_error()
     oob = (ctypes.c_int32 * 1)(4)
-    assert lib.rt_select_blocks(ctypes.byref(sh), p, p, oob, 1, p, None, p, need, None) == rettn.RT_E_ARG
+    assert lib.rt_select_blocks(ctypes.byref(sh), q, k, oob, 1, ix, None, ws, need, None) == rettn.RT_E_ARG
+    assert b"outside" in lib.rt_last_error()
+    ok = (ctypes.c_int32 * 1)(3)
+    assert _passes_validation(lib.rt_select_blocks(ctypes.byref(sh), q, k, ok, 1, ix, None, ws, need, None))
+
+
+def test_overlapping_buffers_are_rejected():
+    """Outputs that overlap inputs (or each other) are RT_E_ARG, named in the
+    error text; the one allowed sharing is calibrating from the layer's own list."""
+    lib = rettn.lib()
+    sh = rettn.shape(1, 2, 200, 64, 64, 2)
+    tbytes = 2 * 200 * 64 * 2
+    q, k, v, o, ix, ws, sc = _addrs(7)
+    need = rettn.select_workspace_bytes(sh)
+    S = ctypes.byref(sh)
+
+    def sel(q_, k_, ix_, sc_, ws_):
+        return lib.rt_select_blocks(S, q_, k_, None, 0, ix_, sc_, ws_, need, None)
+    assert sel(q, k, q, None, ws) == rettn.RT_E_ARG and b"block_idx overlaps q" in lib.rt_last_error()
+    assert sel(q, k, ix, None, ctypes.c_void_p(k.value + tbytes - 16)) == rettn.RT_E_ARG
+    assert b"workspace overlaps k" in lib.rt_last_error()
+    assert sel(q, k, ix, ix, ws) == rettn.RT_E_ARG and b"overlaps" in lib.rt_last_error()
+    assert _passes_validation(sel(q, k, ix, sc, ws))
+    assert _passes_validation(sel(q, k, ix, ctypes.c_void_p(ix.value + 2 * 4 * 2 * 4), ws))  # just past the lists
+
+    nbytes = rettn.stats_cache_bytes(sh, 2)
+    buf, addr = _fake_dev_memory(nbytes)
+    h = ctypes.c_void_p()
+    assert lib.rt_stats_cache_init(ctypes.byref(h), S, 2, ctypes.c_void_p(addr), nbytes) == 0
+    view = rettn.RtStatsView()
+    assert lib.rt_stats_cache_view(h, 1, ctypes.byref(view)) == 0
+    assert lib.rt_calibrate(S, q, k, v, ix, h, 1, q, None) == rettn.RT_E_ARG
+    assert b"o overlaps q" in lib.rt_last_error()
+    assert lib.rt_calibrate(S, q, k, v, ix, h, 1, ctypes.c_void_p(view.R), None) == rettn.RT_E_ARG
+    assert b"cache layer" in lib.rt_last_error()
+    assert lib.rt_calibrate(S, q, k, v, ix, h, 1, ix, None) == rettn.RT_E_ARG  # o over the list it reads
+    assert lib.rt_calibrate(S, q, k, v, ctypes.c_void_p(view.m), h, 1, o, None) == rettn.RT_E_ARG
+    assert _passes_validation(lib.rt_calibrate(S, q, k, v, ctypes.c_void_p(view.idx), h, 1, o, None))
+    assert _passes_validation(lib.rt_calibrate(S, q, k, v, ix, h, 1, o, None))
+    lib.rt_stats_cache_set_valid(h, 1, 1)
+    for bad_o in (v, ctypes.c_void_p(view.m), ix):
+        assert lib.rt_sparse_attn_reshape(S, q, k, v, ix, h, 1, bad_o, None) == rettn.RT_E_ARG
+        assert b"overlaps" in lib.rt_last_error()
+    assert _passes_validation(lib.rt_sparse_attn_reshape(S, q, k, v, ctypes.c_void_p(view.idx), h, 1, o, None))
+    assert _passes_validation(lib.rt_sparse_attn_reshape(S, q, k, v, None, h, 1, o, None))
+    lib.rt_stats_cache_destroy(h)
+    del buf
 
 
 def test_state_machine_without_gpu():
@@ -237,8 +296,8 @@ def test_no_device_is_reported_not_faked():
         pytest.skip("a GPU is present")
     lib = rettn.lib()
     sh = rettn.shape(1, 1, 128, 64, 64, 1)
-    p = ctypes.c_void_p(4096)
-    st = lib.rt_select_blocks(ctypes.byref(sh), p, p, None, 0, p, None, p, 1 << 20, None)
+    q, k, ix, ws = _addrs(4)
+    st = lib.rt_select_blocks(ctypes.byref(sh), q, k, None, 0, ix, None, ws, 1 << 20, None)
     assert st == rettn.RT_E_DEVICE
 
 

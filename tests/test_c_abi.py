@@ -16,7 +16,7 @@ def test_header_is_c_and_host_calls_work(tmp_path):
     exe = tmp_path / "c_abi_check"
     libdir = os.path.dirname(rettn.LIB_PATH)
     cmd = ["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
-           os.path.join(ROOT, "tests", "c_abi_check.c"), "-o", str(exe), "-L", libdir, "-lrettn",
+           os.path.join(ROOT, "tests", "c_abi_check.c"), "-o", str(exe), rettn.LIB_PATH,
            "-Wl,-rpath," + libdir]
     subprocess.run(cmd, check=True, capture_output=True, text=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)

@@ -51,6 +51,9 @@ def block_constant_inputs(B, H, N, D, seed, dtype):
     (65536, 9, [0, 1, 2, 3], "bf16"), (640, 10, [], "bf16"), (130, 1, [2], "bf16"),
     # more than 32 non-forced winners: the bitonic-sort path (and every block kept in the second case)
     (64 * 100, 45, [3], "bf16"), (64 * 40, 40, [0], "bf16"), (64 * 600 + 17, 40, [], "bf16"),
+    # 257..320 key blocks: five 64-block chunks per lane sorted in a 512-key buffer
+    (64 * 278, 40, [0, 1, 2, 3], "bf16"), (64 * 300, 300, [], "bf16"), (64 * 260 + 5, 100, [5], "bf16"),
+    (64 * 278 + 48 - 64, 9, [0, 1, 2, 3], "bf16"),
 ])
 def test_selector_exact_on_exact_scores(N, keep, forced, dtype):
     say("selector exact", N, keep, forced, dtype)
@@ -489,6 +492,42 @@ def test_sparse_many_blocks_per_workgroup(keep, variant):
                                        r32[b, h, rows], N, d))
                 got.append(oh[b, h, rows])
     gu.assert_close(np.concatenate(got), np.concatenate(ref))
+
+
+@pytest.mark.parametrize("dtype,D,d", [("bf16", 64, 64), ("bf16", 80, 72), ("f32", 64, 64)])
+def test_repeated_list_entries_count_once(dtype, D, d):
+    """A non-decreasing list with repeated entries is read as the set of its
+    blocks by calibration and by both sparse epilogues (bf16 and float32), as
+    by the oracle; the list copy in the cache keeps the repeats."""
+    say("repeated list entries", dtype, D)
+    B, H, N, keep = 1, 2, 64 * 20 + 7, 6
+    nb = (N + 63) // 64
+    g = np.random.default_rng(D)
+    idx = np.empty((B, H, nb, keep), dtype=np.int32)
+    for h in range(H):
+        for i in range(nb):
+            picks = np.sort(g.choice(nb, 3, replace=False))
+            row = np.sort(np.concatenate([picks, g.choice(picks, keep - 3)]))  # 3 distinct blocks, 3 repeats
+            idx[0, h, i] = row
+    idx[0, 0, 0] = [nb - 1] * keep  # one block only, the short last one
+    q0, k0, v0 = synth.random_qkv(B, H, N, d, D, seed=90, scale=1.5, dtype=dtype, device=gu.DEV)
+    q1, k1, v1 = synth.random_qkv(B, H, N, d, D, seed=91, scale=1.5, dtype=dtype, device=gu.DEV)
+    sh = rettn.shape(B, H, N, d, D, keep, dtype)
+    cache = rettn.StatsCache(sh, 1)
+    didx = torch.as_tensor(idx).to(gu.DEV)
+    o_cal = gu.calibrate(sh, q0, k0, v0, didx, cache)
+    outs = {var: gu.sparse(sh, q1, k1, v1, cache, variant=var) for var in ("r1", "r2")}
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.tensors(0)["idx"].cpu().numpy(), idx)
+    ref_cal = oracle.calibrate(gu.host(q0), gu.host(k0), gu.host(v0), idx, N, d)
+    tol = dict(max_rel=1e-5, l1_rel=1e-6) if dtype == "f32" else {}
+    gu.assert_close(gu.host(o_cal), ref_cal["o"], what="calibrate", **tol)
+    t = cache.tensors(0)
+    assert np.abs(gu.host(t["z_sparse"]) / ref_cal["z_sparse"] - 1).max() <= 1e-4
+    for var, o in outs.items():
+        ref = oracle_layer(var)(gu.host(q1), gu.host(k1), gu.host(v1), idx, ref_cal, N, d)
+        gu.assert_close(gu.host(o), ref, what=f"sparse {var}", **tol)
+    cache.close()
 
 
 def test_deterministic_bitwise():
