@@ -38,7 +38,12 @@ def block_mask(idx, N):
 
 
 def rel(a, b):
-    return float(np.abs(np.asarray(a) - np.asarray(b)).max() / max(1e-300, np.abs(np.asarray(b)).max()))
+    """Max-relative difference; any non-finite value is an infinite error (a
+    NaN would otherwise vanish inside Python's max of several errors)."""
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    if not (np.all(np.isfinite(a)) and np.all(np.isfinite(b))):
+        return float("inf")
+    return float(np.abs(a - b).max() / max(1e-300, np.abs(b).max()))
 
 
 def small_case(N=200, d=24, D=32, B=1, H=2, keep=2, seed=3, scale=1.0):
@@ -206,6 +211,20 @@ def pin_selector(orc):
     return float(bad)
 
 
+def pin_dense_attention(orc):
+    """The oracle's dense attention equals library SDPA: ragged N, a true head
+    dim of 72 stored padded to 80 (zero channels), several (b, h), and logits
+    large enough that an unshifted exponential would overflow."""
+    errs = []
+    for N, d, D, scale in ((201, 72, 80, 1.0), (130, 16, 16, 24.0), (64, 64, 64, 0.5)):
+        q, k, v = (t.numpy().astype(np.float64) for t in synth.random_qkv(2, 3, N, d, D, seed=N + d, scale=scale))
+        o = orc.dense_attention(q, k, v, N, d)
+        errs.append(rel(o, sdpa64(q, k, v, N, d)))
+        if D > d:
+            errs.append(float(np.abs(o[..., d:]).max()))
+    return max(errs)
+
+
 # ---------------------------------------------------------------- reshape variant R2
 def pin_r2_calibration_identity(orc):
     """R2 on the calibration inputs gives dense attention (as R1 does)."""
@@ -272,6 +291,7 @@ ALL_PINS = {
     "pooling": (pin_pooling, 1e-12),
     "pooled_scores": (pin_pooled_scores, 1e-12),
     "selector": (pin_selector, 0.0),
+    "dense_attention": (pin_dense_attention, 1e-10),
     "r2_calibration_identity": (pin_r2_calibration_identity, 1e-10),
     "r2_keep_all": (pin_r2_keep_all, 1e-10),
     "r2_closed_form": (pin_r2_closed_form, 1e-10),
@@ -284,7 +304,8 @@ def failing_pins(orc):
     out = []
     for name, (fn, tol) in ALL_PINS.items():
         try:
-            err = fn(orc)
+            with np.errstate(all="ignore"):  # broken copies may overflow
+                err = fn(orc)
             if not (err <= tol):
                 out.append(name)
         except Exception:  # a broken oracle may also crash

@@ -10,11 +10,16 @@ from tests import hilbert_pins
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "hilbert.py")
 
 MUTATIONS = {
-    "reflect_and_swap_exchanged": ("            if x[i] & q:\n", "            if not x[i] & q:\n"),
-    "gray_across_axes_skipped": ("        x[i] ^= x[i - 1]\n", "        pass\n"),
-    "level_flip_skipped": ("    for i in range(n):\n        x[i] ^= flip\n", ""),
-    "interleave_axes_reversed": ("h = (h << 1) | ((x[i] >> b) & 1)", "h = (h << 1) | ((x[n - 1 - i] >> b) & 1)"),
-    "levels_interleaved_low_first": ("for b in range(bits - 1, -1, -1):", "for b in range(bits):"),
+    "gray_code_not_reflected": ("g = j ^ (j >> 1)", "g = j"),
+    "axis0_least_significant": ("(g >> (n - 1 - a)) & 1", "(g >> a) & 1"),
+    "first_quarter_not_mirrored": ("((1, 0), (0, 0)),  # (0,0)", "((0, 1), (0, 0)),  # (0,0)"),
+    "last_quarter_not_flipped": ("((1, 0), (1, 1)),  # (1,0)", "((1, 0), (0, 0)),  # (1,0)"),
+    "3d_first_piece_unrotated": ("((2, 0, 1), (0, 0, 0)),  # (0,0,0)", "((0, 1, 2), (0, 0, 0)),  # (0,0,0)"),
+    "3d_fourth_piece_unflipped": ("((2, 1, 0), (1, 0, 1)),  # (0,1,0)", "((2, 1, 0), (0, 0, 0)),  # (0,1,0)"),
+    "3d_seventh_piece_wrong_axes": ("((1, 0, 2), (1, 1, 0)),  # (1,0,1)", "((0, 1, 2), (1, 1, 0)),  # (1,0,1)"),
+    "child_transform_skipped": ("hilbert_index(back, bits - 1)", "hilbert_index(y, bits - 1)"),
+    "flip_over_the_whole_side": ("s - 1 - y[perm[a]] if flip[a]", "2 * s - 1 - y[perm[a]] if flip[a]"),
+    "piece_weight_wrong": ("return j * s ** n +", "return j * s +"),
     "enclosing_cube_too_small": ("while any(s > (1 << k) for s in dims):", "while any(s > (2 << k) for s in dims):"),
     "not_sorted": ('order = np.argsort(keys, kind="stable")', "order = np.arange(len(keys))"),
     "text_moved_last": ("np.concatenate([np.arange(n_text), n_text + order])",

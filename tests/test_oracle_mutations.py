@@ -34,6 +34,15 @@ MUTATIONS = {
     "r2_residual_over_sparse_denominator": ("+ r_c / z_full_c[:, None]", "+ r_c / z_sparse_c[:, None]"),
     "r2_sparse_output_unnormalised": ("o_sparse = (p @ V) / p.sum(axis=1)[:, None]", "o_sparse = p @ V"),
     "r2_residual_dropped": ("* o_sparse + r_c / z_full_c[:, None]", "* o_sparse"),
+    # dense attention (the reference of the GPU identity tests)
+    "dense_scale_uses_d_not_sqrt": ("alpha = dtype(1.0) / np.sqrt(dtype(d))\n    o = np.zeros(",
+                                    "alpha = dtype(1.0) / dtype(d)\n    o = np.zeros("),
+    "dense_max_over_wrong_axis": ("p = np.exp(s - s.max(axis=1, keepdims=True))",
+                                  "p = np.exp(s - s.max(axis=0, keepdims=True))"),
+    "dense_max_not_subtracted": ("p = np.exp(s - s.max(axis=1, keepdims=True))", "p = np.exp(s)"),
+    "dense_normalised_by_max": ("(p @ V) / p.sum(axis=1, keepdims=True)", "(p @ V) / p.max(axis=1, keepdims=True)"),
+    "dense_values_misaligned": ("K, V = k[b, h, :N], v[b, h, :N]", "K, V = k[b, h, :N], v[b, h, :N][::-1]"),
+    "dense_keys_of_own_block_only": ("s = alpha * (q[b, h, a:e] @ K.T)", "s = alpha * (q[b, h, a:e] @ K[a:e].T)"),
 }
 
 
