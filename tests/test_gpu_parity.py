@@ -524,9 +524,12 @@ def test_repeated_list_entries_count_once(dtype, D, d):
     gu.assert_close(gu.host(o_cal), ref_cal["o"], what="calibrate", **tol)
     t = cache.tensors(0)
     assert np.abs(gu.host(t["z_sparse"]) / ref_cal["z_sparse"] - 1).max() <= 1e-4
+    # the sparse steps read the GPU's own float32 calibration (L1 error about
+    # 1e-6 already), so the two-step chain is held to 3e-6 in float32
+    tol2 = dict(max_rel=1e-5, l1_rel=3e-6) if dtype == "f32" else {}
     for var, o in outs.items():
         ref = oracle_layer(var)(gu.host(q1), gu.host(k1), gu.host(v1), idx, ref_cal, N, d)
-        gu.assert_close(gu.host(o), ref, what=f"sparse {var}", **tol)
+        gu.assert_close(gu.host(o), ref, what=f"sparse {var}", **tol2)
     cache.close()
 
 
