@@ -140,6 +140,26 @@ rt_status rt_select_blocks(const rt_shape* shape, const void* q, const void* k,
                            int32_t* block_idx, float* pooled_scores,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- the same selector without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation) ----
+ * Computes exactly what rt_select_blocks computes (the same kernels), with the
+ * pooled means in scratch memory the library holds: one static device array
+ * of RT_SELECT_SCRATCH_BYTES per GPU, from the first call on that GPU until
+ * the process ends.  The call allocates and frees nothing.  A shape whose
+ * rt_select_workspace_bytes exceeds RT_SELECT_SCRATCH_BYTES returns
+ * RT_E_WORKSPACE before touching the device (16 MiB covers B*H*Nb*d_pad up to
+ * 2M, e.g. 96 heads of 17776 tokens at d_pad 64).  Every call on one GPU uses
+ * that GPU's one array and it keeps the last call's contents: calls that
+ * overlap in time on one GPU (several streams or threads) race and give
+ * unspecified lists; calls ordered on one stream are safe.  Nothing in the
+ * scratch needs to start at zero: each call writes every byte it reads.
+ * Other arguments and errors as for rt_select_blocks.                       */
+#define RT_SELECT_SCRATCH_BYTES (16u << 20)
+rt_status rt_select_blocks_noalloc(const rt_shape* shape, const void* q, const void* k,
+                                   const int32_t* forced, int32_t n_forced,
+                                   int32_t* block_idx, float* pooled_scores, void* stream);
+
 /* ---- statistics cache (teaser paragraph: statistics cached across denoising steps) ----
  * rt_stats_cache_bytes : device bytes for n_layers layers of `shape`.
  * rt_stats_cache_init  : wraps caller-owned device memory `dev_mem` of `bytes`;

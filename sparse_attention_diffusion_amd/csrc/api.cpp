@@ -272,6 +272,25 @@ rt_status rt_select_blocks(const rt_shape* s, const void* q, const void* k, cons
   return launched(rettn::launch_select(s->dtype == RT_BF16, s->d_pad, a, hs), hs, "rt_select_blocks");
 }
 
+rt_status rt_select_blocks_noalloc(const rt_shape* s, const void* q, const void* k, const int32_t* forced,
+                                   int32_t n_forced, int32_t* block_idx, float* pooled_scores, void* stream) {
+  static_assert(rettn::kSelectScratchBytes == (size_t)RT_SELECT_SCRATCH_BYTES, "scratch size");
+  rt_status st = check_shape(s);
+  if (st != RT_OK) return st;
+  if (is_empty(s)) return RT_OK;
+  if (select_ws(s) > rettn::kSelectScratchBytes)
+    return fail(RT_E_WORKSPACE,
+                "the selector needs %zu bytes of scratch; the allocation-free entry point holds %zu "
+                "(use rt_select_blocks with a workspace)",
+                select_ws(s), rettn::kSelectScratchBytes);
+  if ((st = check_device()) != RT_OK) return st;
+  void* scratch = nullptr;
+  const hipError_t e = rettn::select_scratch(&scratch);
+  if (e != hipSuccess) return fail(RT_E_DEVICE, "selector scratch: %s", hipGetErrorString(e));
+  return rt_select_blocks(s, q, k, forced, n_forced, block_idx, pooled_scores, scratch, rettn::kSelectScratchBytes,
+                          stream);
+}
+
 size_t rt_stats_cache_bytes_ex(const rt_shape* s, int32_t n_layers, int32_t residual_dtype) {
   if (check_shape(s) != RT_OK || n_layers < 1) return 0;
   if (residual_dtype != RT_F32 && !(residual_dtype == RT_BF16 && s->dtype == RT_BF16)) return 0;

@@ -68,4 +68,10 @@ hipError_t launch_attn_bf16(AttnMode mode, int D, const AttnArgs& a, hipStream_t
 hipError_t launch_attn_f32(AttnMode mode, int D, const AttnArgs& a, hipStream_t s);
 hipError_t launch_select(bool bf16, int D, const SelectArgs& a, hipStream_t s);
 
+// Scratch of the allocation-free selector: a static device array of this many
+// bytes (select.hip) holding the pooled means.  select_scratch returns its
+// address on the current device, looked up once per device.
+constexpr size_t kSelectScratchBytes = size_t(16) << 20;
+hipError_t select_scratch(void** ptr);
+
 }  // namespace rettn

@@ -21,9 +21,38 @@
 //                   maximum of 64-bit (score, ~index) keys, and the list is
 //                   written in ascending order through a flag row and ballots.
 //                   Large selections fall back to a bitonic sort in LDS.
+#include <mutex>
+#include <vector>
+
 #include "internal.h"
 
 namespace rettn {
+
+// Pooled means of the allocation-free entry point (rt_select_blocks_noalloc).
+// Each GPU the library runs on holds its own copy until the process ends.  In
+// host code this name is only a stand-in for the symbol: the device address
+// comes from select_scratch() and is the only form passed to kernels.
+static __device__ __align__(256) char scratch[kSelectScratchBytes];
+
+hipError_t select_scratch(void** out) {
+  static std::mutex mu;
+  static std::vector<void*> ptrs;  // per device id
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)ptrs.size() <= dev) ptrs.resize(dev + 1, nullptr);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
+}
+
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));

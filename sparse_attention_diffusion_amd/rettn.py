@@ -18,6 +18,7 @@ RT_OK, RT_E_ARG, RT_E_SHAPE, RT_E_DTYPE, RT_E_STATE, RT_E_WORKSPACE, RT_E_LAUNCH
 RT_BF16, RT_F32 = 0, 1
 _DTYPES = {"bf16": RT_BF16, "f32": RT_F32}
 BLOCK = 64
+SELECT_SCRATCH_BYTES = 16 << 20  # RT_SELECT_SCRATCH_BYTES
 
 
 class RtShape(ctypes.Structure):
@@ -48,6 +49,7 @@ def _load():
         "rt_num_blocks": (I32, [S]),
         "rt_select_workspace_bytes": (SZ, [S]),
         "rt_select_blocks": (I32, [S, P, P, ctypes.POINTER(I32), I32, P, P, P, SZ, P]),
+        "rt_select_blocks_noalloc": (I32, [S, P, P, ctypes.POINTER(I32), I32, P, P, P]),
         "rt_stats_cache_bytes": (SZ, [S, I32]),
         "rt_stats_cache_init": (I32, [ctypes.POINTER(P), S, I32, P, SZ]),
         "rt_stats_cache_bytes_ex": (SZ, [S, I32, I32]),
@@ -82,7 +84,7 @@ SYMBOLS = [
     "rt_stats_cache_init_ex", "rt_stats_cache_view",
     "rt_stats_cache_set_valid", "rt_stats_cache_invalidate", "rt_stats_cache_destroy", "rt_calibrate",
     "rt_sparse_attn_reshape", "rt_sparse_attn_reshape_ex", "rt_schedule_is_calibration", "rt_step_workspace_bytes", "rt_attention_step",
-    "rt_attention_step_ex", "rt_hilbert_order", "rt_permute_rows",
+    "rt_attention_step_ex", "rt_hilbert_order", "rt_permute_rows", "rt_select_blocks_noalloc",
 ]
 
 
@@ -156,6 +158,13 @@ def rt_select_blocks(sh, q, k, forced, block_idx, pooled_scores, workspace, stre
                                  _ptr(pooled_scores), _ptr(workspace),
                                  0 if workspace is None else workspace.numel() * workspace.element_size(),
                                  _stream(stream)))
+
+
+def rt_select_blocks_noalloc(sh, q, k, forced, block_idx, pooled_scores, stream=None):
+    """rt_select_blocks with the pooled means in the library's own scratch (no workspace)."""
+    arr, n = _forced_arr(forced)
+    _check(_lib.rt_select_blocks_noalloc(ctypes.byref(sh), _ptr(q), _ptr(k), arr if n else None, n,
+                                         _ptr(block_idx), _ptr(pooled_scores), _stream(stream)))
 
 
 class StatsCache:

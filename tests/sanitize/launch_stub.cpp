@@ -13,5 +13,6 @@ hipError_t launch_permute(const PermuteArgs&, hipStream_t) { return hipErrorNoDe
 hipError_t launch_attn_bf16(AttnMode, int, const AttnArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_attn_f32(AttnMode, int, const AttnArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_select(bool, int, const SelectArgs&, hipStream_t) { return hipErrorNoDevice; }
+hipError_t select_scratch(void**) { return hipErrorNoDevice; }
 
 }  // namespace rettn

@@ -200,6 +200,27 @@ def test_select_argument_errors():
     assert _passes_validation(lib.rt_select_blocks(ctypes.byref(sh), q, k, ok, 1, ix, None, ws, need, None))
 
 
+def test_noalloc_selector_limit():
+    """The allocation-free selector refuses shapes whose pooled means exceed its
+    16 MiB scratch, before any device call; the headline shapes fit."""
+    lib = rettn.lib()
+    text = open(os.path.join(ROOT, "include", "rettn.h")).read()
+    assert "#define RT_SELECT_SCRATCH_BYTES (16u << 20)" in text and rettn.SELECT_SCRATCH_BYTES == 16 << 20
+    q, k, ix = _addrs(3)
+    big = rettn.shape(2, 64, 65536, 64, 64, 9)
+    assert rettn.select_workspace_bytes(big) > rettn.SELECT_SCRATCH_BYTES
+    assert lib.rt_select_blocks_noalloc(ctypes.byref(big), q, k, None, 0, ix, None, None) == rettn.RT_E_WORKSPACE
+    assert b"allocation-free" in lib.rt_last_error()
+    for B, H in ((2, 30), (2, 48)):
+        sh = rettn.shape(B, H, 17776, 64, 64, 9)
+        assert rettn.select_workspace_bytes(sh) <= rettn.SELECT_SCRATCH_BYTES
+        assert _passes_validation(lib.rt_select_blocks_noalloc(ctypes.byref(sh), q, k, None, 0, ix, None, None))
+    bad = rettn.shape(1, 1, 100, 64, 64, 0)
+    assert lib.rt_select_blocks_noalloc(ctypes.byref(bad), q, k, None, 0, ix, None, None) == rettn.RT_E_SHAPE
+    empty = rettn.shape(0, 1, 100, 64, 64, 1)
+    assert lib.rt_select_blocks_noalloc(ctypes.byref(empty), None, None, None, 0, None, None, None) == 0
+
+
 def test_overlapping_buffers_are_rejected():
     """Outputs that overlap inputs (or each other) are RT_E_ARG, named in the
     error text; the one allowed sharing is calibrating from the layer's own list."""
