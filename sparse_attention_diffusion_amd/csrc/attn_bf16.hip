@@ -861,8 +861,12 @@ struct CalibCtx {
   Dma dma;
   Frag<D> fr;
   Rows<D> st;
-  f32x16 okept[NT], ores[NT];
-  float zk, zm;
+  // Every key block is added to the all-keys accumulator (in place, the same
+  // registers each step); kept blocks are also added to the kept accumulator.
+  // The residual is the difference at the end: with every block kept the two
+  // see identical operations, so R = 0 and Z_sparse = Z_full exactly.
+  f32x16 oall[NT], okept[NT];
+  float zall, zk;
 
   template <int SLOT>
   __device__ __forceinline__ void step(int j) {
@@ -880,24 +884,31 @@ struct CalibCtx {
     bool any;
     const float corr = update_max(st.m_ref, st.m_true, row_max(s), c, &any);
     if (any) {
+      zall *= corr;
       zk *= corr;
-      zm *= corr;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
+        oall[t] *= corr;
         okept[t] *= corr;
-        ores[t] *= corr;
       }
     }
     bf16x8 p[2][2];
-    const float zb = probs(p, s, st.m_ref, c);
-    if (kept) {
-      zk += zb;
-      if constexpr (D == 80) pv_lean<D, SLOT * Shape<D>::SLOT>(okept, p, fr);
-      else pv<D, SLOT * Shape<D>::SLOT>(okept, p, fr);
+    const float zb = probs(p, s, st.m_ref, c);  // float32 sums of the exact exponentials
+    zall += zb;
+    if constexpr (D == 80) {
+      pv_lean<D, SLOT * Shape<D>::SLOT>(oall, p, fr);
+      if (kept) {
+        zk += zb;
+        pv_lean<D, SLOT * Shape<D>::SLOT>(okept, p, fr);
+      }
     } else {
-      zm += zb;
-      if constexpr (D == 80) pv_lean<D, SLOT * Shape<D>::SLOT>(ores, p, fr);
-      else pv<D, SLOT * Shape<D>::SLOT>(ores, p, fr);
+      u32x2 h[NT][2][2][2];
+      v_fetch<D, SLOT * Shape<D>::SLOT>(h, fr);
+      pv_mfma<D>(oall, p, h);
+      if (kept) {
+        zk += zb;
+        pv_mfma<D>(okept, p, h);
+      }
     }
   }
 };
@@ -948,8 +959,8 @@ calib_kernel(AttnArgs a, XcdGrid grid) {
   cx.dma.init(wave, lane);
   cx.fr.init(ring);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) cx.okept[t] = cx.ores[t] = f32x16{};
-  cx.zk = cx.zm = 0.f;
+  for (int t = 0; t < NT; ++t) cx.oall[t] = cx.okept[t] = f32x16{};
+  cx.zall = cx.zk = 0.f;
   __syncthreads();  // flags and Q in place
 
 #pragma unroll
@@ -966,7 +977,7 @@ calib_kernel(AttnArgs a, XcdGrid grid) {
   // Statistics relative to the true row max m: factor e^{m_ref - m}.
   const float f = __builtin_amdgcn_exp2f((cx.st.m_ref - cx.st.m_true) * cx.c);
   const float zs = pair_sum(cx.zk) * f;
-  const float zf = zs + pair_sum(cx.zm) * f;
+  const float zf = pair_sum(cx.zall) * f;
   if (row_ok) {
     const size_t srow = (size_t)bh * N + row;
     if (g == 0) {
@@ -986,8 +997,8 @@ calib_kernel(AttnArgs a, XcdGrid grid) {
           __bf16 ob[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            r[e] = cx.ores[t][4 * i4 + e] * f;
-            ob[e] = (__bf16)((cx.okept[t][4 * i4 + e] * f + r[e]) * inv);
+            r[e] = (cx.oall[t][4 * i4 + e] - cx.okept[t][4 * i4 + e]) * f;
+            ob[e] = (__bf16)(cx.oall[t][4 * i4 + e] * f * inv);
           }
           if (RB) {  // residual rounded to bf16 (nearest even)
             __bf16 rb[4];
