@@ -28,6 +28,32 @@ def assert_close(got, ref, max_rel=MAX_REL, l1_rel=L1_REL, what="O"):
     return mx, l1
 
 
+class Worst:
+    """Collects per-block errors of one compared step; check() asserts the
+    tolerance on every block and prints the worst block of the step."""
+
+    def __init__(self, what, max_rel=MAX_REL, l1_rel=L1_REL):
+        self.what, self.max_rel, self.l1_rel = what, max_rel, l1_rel
+        self.rows = []
+
+    def add(self, got, ref, where):
+        got = np.asarray(got, dtype=np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        finite = bool(np.all(np.isfinite(got)))
+        mx, l1 = errors(got, ref) if finite else (float("inf"), float("inf"))
+        self.rows.append((mx, l1, where))
+
+    def check(self):
+        assert self.rows, f"{self.what}: nothing compared"
+        wm = max(self.rows, key=lambda r: r[0])
+        wl = max(self.rows, key=lambda r: r[1])
+        print(f"[err] {self.what}: {len(self.rows)} blocks, worst max-rel {wm[0]:.3e} at {wm[2]}, "
+              f"worst L1-rel {wl[1]:.3e} at {wl[2]}", flush=True)
+        bad = [r for r in self.rows if not (r[0] <= self.max_rel and r[1] <= self.l1_rel)]
+        assert not bad, f"{self.what}: {len(bad)} blocks out of tolerance, e.g. {bad[:3]}"
+        return wm[0], wl[1]
+
+
 def host(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 

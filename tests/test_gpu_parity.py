@@ -230,10 +230,83 @@ def run_sampled_parity(cfg, heads, seed=0, n_steps=2, check_steps=(1,), residual
     cache.close()
 
 
-def test_parity_cogvideox2b_sampled():
-    say("parity cogvideox2b sampled")
+def host32(t):
+    """A whole device tensor as a float32 host array (converted per head later)."""
+    return t.detach().float().cpu().numpy()
+
+
+def check_stats(t, b, h, rows, st, where):
+    m = gu.host(t["m"][b, h, rows])
+    assert np.abs(m - st["m"]).max() <= 1e-4 * max(1.0, np.abs(st["m"]).max()), ("m", where)
+    for zname in ("z_full", "z_sparse"):
+        assert np.abs(gu.host(t[zname][b, h, rows]) / st[zname] - 1).max() <= 1e-4, (zname, where)
+    r = gu.host(t["R"][b, h, rows])
+    assert np.abs(r - st["r"]).sum() <= 3e-3 * max(1e-30, np.abs(st["r"]).sum()), ("R", where)
+
+
+def test_parity_cogvideox2b_all_heads():
+    """cogvideox2b at full size through its whole 50-step schedule.  The
+    oracle's lists for every head drive a calibration at step 0; the oracle
+    checks, on all 60 (b, h), the first, text/video boundary, first video,
+    middle and ragged last query blocks at the calibration step and at steps
+    1, 25 and 49, and every query block of two heads at steps 0 and 49."""
+    say("parity cogvideox2b all heads")
     cfg = configs.CONFIGS["cogvideox2b"]
-    run_sampled_parity(cfg, heads=[(0, 0), (1, 29)], n_steps=4, check_steps=(1, 3))
+    sh = rettn.shape_of(cfg)
+    N, d, keep = cfg["N"], cfg["d"], cfg["keep"]
+    forced = configs.forced_blocks(cfg)
+    nb = configs.n_blocks(N)
+    full_heads = [(0, 0), (1, 29)]
+    sampled = gu.sample_blocks(nb)
+    units = sorted({(b, h, i) for b in range(sh.B) for h in range(sh.H) for i in sampled}
+                   | {(b, h, i) for b, h in full_heads for i in range(nb)})
+    full_only = {(b, h, i) for b, h in full_heads for i in range(nb)} - {(b, h, i) for b, h, i in units
+                                                                          if i in sampled}
+    it = synth.StepInputs(cfg, seed=0, device=gu.DEV)
+    q0, k0, v0 = it.next_stored()
+    hq, hk, hv = host32(q0), host32(k0), host32(v0)
+    ref_idx = oracle.select_blocks(hq, hk, N, d, keep, forced)  # every head
+    cache = rettn.StatsCache(sh, 1)
+    o = gu.calibrate(sh, q0, k0, v0, torch.as_tensor(ref_idx).to(gu.DEV), cache)
+    torch.cuda.synchronize()
+    t = cache.tensors(0)
+    assert np.array_equal(t["idx"].cpu().numpy(), ref_idx)
+    ho = host32(o)
+    refs = {}
+    w = gu.Worst("cogvideox2b calibration")
+    for b in range(sh.B):
+        for h in range(sh.H):
+            kh, vh = hk[b, h].astype(np.float64), hv[b, h].astype(np.float64)
+            qh = hq[b, h].astype(np.float64)
+            for i in (i for (bb, hh, i) in units if (bb, hh) == (b, h)):
+                rows = gu.block_rows(N, i)
+                st = oracle.calibrate_rows(qh, kh, vh, rows, ref_idx[b, h, i], N, d)
+                refs[b, h, i] = st
+                w.add(ho[b, h, rows], st["o"], (b, h, i))
+                check_stats(t, b, h, rows, st, (b, h, i))
+    w.check()
+    for s in range(1, 50):
+        q, k, v = it.next_stored()
+        if s not in (1, 25, 49):
+            continue
+        o = gu.sparse(sh, q, k, v, cache)
+        torch.cuda.synchronize()
+        hq, hk, hv, ho = host32(q), host32(k), host32(v), host32(o)
+        w = gu.Worst(f"cogvideox2b step {s}")
+        for b in range(sh.B):
+            for h in range(sh.H):
+                kh, vh = hk[b, h].astype(np.float64), hv[b, h].astype(np.float64)
+                qh = hq[b, h].astype(np.float64)
+                for (bb, hh, i) in units:
+                    if (bb, hh) != (b, h) or (s != 49 and (b, h, i) in full_only):
+                        continue
+                    rows = gu.block_rows(N, i)
+                    st = refs[b, h, i]
+                    ro = oracle.sparse_reshape_rows(qh, kh, vh, rows, ref_idx[b, h, i], st["m"], st["z_full"],
+                                                    st["z_sparse"], st["r"], N, d)
+                    w.add(ho[b, h, rows], ro, (b, h, i))
+        w.check()
+    cache.close()
 
 
 def test_parity_pixart1024_bf16_residual():
@@ -615,55 +688,77 @@ def test_schedule_with_reselection(variant):
     cache.close()
 
 
-def test_cogvideox5b_layers_and_recalibration():
-    """42 layers share one cache allocation; layers 0 and 41 run a 12-step
-    schedule with recalibration every 10 steps; sampled rows of the
-    recalibration step and the step after it are checked."""
-    say("cogvideox5b 42-layer cache")
+def test_cogvideox5b_full_schedule():
+    """cogvideox5b: 42 layers share one cache allocation (19.3 GB); layers 0 and
+    41 run the whole 50-step schedule through rt_attention_step with
+    recalibration (and reselection) every 10 steps.  At every recalibration
+    (0, 10, 20, 30, 40), the step after it and step 49, the oracle checks all
+    96 (b, h) on three query blocks each (the text/video boundary, a middle
+    block that varies with the head, the ragged last): the GPU's lists equal
+    the oracle's (else differ only at a near-tie, and the block is skipped),
+    the calibration output and statistics, and the reshaped sparse outputs."""
+    say("cogvideox5b full schedule")
     cfg = configs.CONFIGS["cogvideox5b"]
     sh = rettn.shape_of(cfg)
-    N, d, keep = cfg["N"], cfg["d"], cfg["keep"]
+    N, d, keep, period = cfg["N"], cfg["d"], cfg["keep"], cfg["period"]
     forced = configs.forced_blocks(cfg)
     nb = configs.n_blocks(N)
     cache = rettn.StatsCache(sh, cfg["layers"])
     ws = torch.empty(rettn.step_workspace_bytes(sh), dtype=torch.uint8, device=gu.DEV)
-    heads = [(0, 0), (1, 47)]
-    blocks = gu.sample_blocks(nb)
+    compare = {0, 1, 10, 11, 20, 21, 30, 31, 40, 41, 49}
+    units = [(b, h, i) for b in range(sh.B) for h in range(sh.H)
+             for i in (3, 5 + (17 * (b * sh.H + h)) % (nb - 6), nb - 1)]
+    n_ties = 0
     for layer in (0, cfg["layers"] - 1):
         it = synth.StepInputs(cfg, seed=1000 + layer, device=gu.DEV)
-        cal_inputs = None
-        for s in range(12):
-            q, k, v = (synth.store(x, cfg["dtype"]) for x in it.next())
+        refs = {}
+        for s in range(cfg["steps"]):
+            q, k, v = it.next_stored()
             o = gu.empty_out(sh)
-            did = rettn.rt_attention_step(sh, q, k, v, forced, cache, layer, s, cfg["period"], o, ws)
+            did = rettn.rt_attention_step(sh, q, k, v, forced, cache, layer, s, period, o, ws)
             torch.cuda.synchronize()
-            assert did == (s in (0, 10))
-            if s < 10:
+            assert did == (s % period == 0)
+            if s not in compare:
                 continue
-            if s == 10:
-                cal_inputs = {bh: [gu.host(x[bh[0], bh[1]]) for x in (q, k, v)] for bh in heads}
-                lists = cache.tensors(layer)["idx"].cpu().numpy()
-            for (b, h) in heads:
-                qc, kc, vc = cal_inputs[b, h]
-                ref_scores = oracle.pooled_scores(qc[None, None], kc[None, None], N, d)[0, 0]
-                for i in blocks:
-                    ref_list = oracle.select_from_scores(ref_scores[i], keep, forced)
-                    if set(lists[b, h, i]) != set(ref_list):  # only a near-tie may differ
-                        tau = min(ref_scores[i, j] for j in ref_list if j not in forced)
-                        assert all(abs(ref_scores[i, j] - tau) < 1e-5 for j in set(lists[b, h, i]) ^ set(ref_list))
-                        continue
-                    rows = gu.block_rows(N, i)
-                    st = oracle.calibrate_rows(qc, kc, vc, rows, ref_list, N, d)
-                    if s == 10:
-                        gu.assert_close(gu.host(o[b, h, rows]), st["o"], what=f"L{layer} s10 b{b}h{h}i{i}")
-                    else:
-                        qh, kh, vh = (gu.host(x[b, h]) for x in (q, k, v))
-                        ro = oracle.sparse_reshape_rows(qh, kh, vh, rows, ref_list, st["m"], st["z_full"],
-                                                        st["z_sparse"], st["r"], N, d)
-                        gu.assert_close(gu.host(o[b, h, rows]), ro, what=f"L{layer} s11 b{b}h{h}i{i}")
+            hq, hk, hv, ho = host32(q), host32(k), host32(v), host32(o)
+            w = gu.Worst(f"cogvideox5b layer {layer} step {s} ({'calibration' if did else 'sparse'})")
+            if did:
+                t = cache.tensors(layer)
+                lists = t["idx"].cpu().numpy()
+                ref_scores = oracle.pooled_scores(hq, hk, N, d)
+                refs = {}
+            for b in range(sh.B):
+                for h in range(sh.H):
+                    kh, vh = hk[b, h].astype(np.float64), hv[b, h].astype(np.float64)
+                    qh = hq[b, h].astype(np.float64)
+                    for (bb, hh, i) in units:
+                        if (bb, hh) != (b, h):
+                            continue
+                        rows = gu.block_rows(N, i)
+                        if did:
+                            ref_list = oracle.select_from_scores(ref_scores[b, h, i], keep, forced)
+                            if set(lists[b, h, i]) != set(ref_list):  # only a near-tie may differ
+                                tau = min(ref_scores[b, h, i, j] for j in ref_list if j not in forced)
+                                assert all(abs(ref_scores[b, h, i, j] - tau) < 1e-5
+                                           for j in set(lists[b, h, i]) ^ set(ref_list)), (layer, s, b, h, i)
+                                n_ties += 1
+                                continue
+                            st = oracle.calibrate_rows(qh, kh, vh, rows, ref_list, N, d)
+                            refs[b, h, i] = (st, ref_list)
+                            w.add(ho[b, h, rows], st["o"], (b, h, i))
+                            check_stats(t, b, h, rows, st, (layer, s, b, h, i))
+                        elif (b, h, i) in refs:
+                            st, ref_list = refs[b, h, i]
+                            ro = oracle.sparse_reshape_rows(qh, kh, vh, rows, ref_list, st["m"], st["z_full"],
+                                                            st["z_sparse"], st["r"], N, d)
+                            w.add(ho[b, h, rows], ro, (b, h, i))
+            w.check()
+    print(f"[case] cogvideox5b: {n_ties} (layer, step, block) lists skipped at near-ties", flush=True)
+    assert n_ties <= len(units)  # near-ties are rare
     views = [cache.tensors(layer) for layer in (0, 1, cfg["layers"] - 1)]
     assert views[0]["valid"] == 1 and views[1]["valid"] == 0 and views[2]["valid"] == 1
     assert not torch.equal(views[0]["m"], views[2]["m"])
+    cache.close()
 
 
 # ------------------------------------------------------------------ token order (Hilbert)
