@@ -128,7 +128,9 @@ int32_t rt_version(void);
 int32_t rt_num_blocks(const rt_shape* shape);
 
 /* ---- block selector (project page, Abstract: attention over a subset of tokens) ----
- * Workspace: float32 pooled means of q and k, 2 * B*H*Nb*d_pad*4 bytes (+ alignment).
+ * Workspace: the float32 means of k's blocks, B*H*Nb*d_pad*4 bytes (rounded up to
+ * 256); rt_select_workspace_bytes gives the size.  The query blocks are pooled
+ * inside the selecting kernel.
  * q, k      : device [B,H,N,d_pad].
  * forced    : HOST array of n_forced distinct block indices in [0, Nb), or NULL.
  *             They are always kept and count toward `keep`.
@@ -144,12 +146,12 @@ rt_status rt_select_blocks(const rt_shape* shape, const void* q, const void* k,
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation) ----
  * Computes exactly what rt_select_blocks computes (the same kernels), with the
- * pooled means in scratch memory the library holds: one static device array
+ * K means in scratch memory the library holds: one static device array
  * of RT_SELECT_SCRATCH_BYTES per GPU, from the first call on that GPU until
  * the process ends.  The call allocates and frees nothing.  A shape whose
  * rt_select_workspace_bytes exceeds RT_SELECT_SCRATCH_BYTES returns
  * RT_E_WORKSPACE before touching the device (16 MiB covers B*H*Nb*d_pad up to
- * 2M, e.g. 96 heads of 17776 tokens at d_pad 64).  Every call on one GPU uses
+ * 4M, e.g. 96 heads of 17776 tokens at d_pad 64).  Every call on one GPU uses
  * that GPU's one array and it keeps the last call's contents: calls that
  * overlap in time on one GPU (several streams or threads) race and give
  * unspecified lists; calls ordered on one stream are safe.  Nothing in the

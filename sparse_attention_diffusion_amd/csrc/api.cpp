@@ -189,10 +189,8 @@ rt_status check_cache(const rt_shape* s, const rt_stats_cache* c, int32_t layer)
   return RT_OK;
 }
 
-size_t select_ws(const rt_shape* s) {
-  const size_t pooled = (size_t)s->B * s->H * nblocks(s->N) * s->d_pad * 4;
-  return 2 * align_up(pooled);
-}
+// The selector's workspace: the float32 means of K, [B*H, d_pad, Nb].
+size_t select_ws(const rt_shape* s) { return align_up((size_t)s->B * s->H * nblocks(s->N) * s->d_pad * 4); }
 
 }  // namespace
 
@@ -256,11 +254,9 @@ rt_status rt_select_blocks(const rt_shape* s, const void* q, const void* k, cons
     a.forced[j >> 5] |= 1u << (j & 31);
   }
   if ((st = check_device()) != RT_OK) return st;
-  const size_t pooled = align_up((size_t)s->B * s->H * nb * s->d_pad * 4);
   a.q = q;
   a.k = k;
-  a.qb = (float*)workspace;
-  a.kb = (float*)((char*)workspace + pooled);
+  a.kb = (float*)workspace;
   a.idx = block_idx;
   a.scores = pooled_scores;
   a.BH = s->B * s->H;

@@ -32,8 +32,7 @@ struct AttnArgs {
 struct SelectArgs {
   const void* q;
   const void* k;
-  float* qb;               // workspace [BH, Nb, D] float32
-  float* kb;
+  float* kb;               // workspace: K means [BH, D, Nb] float32 (transposed)
   int32_t* idx;            // [BH, Nb, keep]
   float* scores;           // [BH, Nb, Nb] or null
   int32_t BH, N, Nb, keep;
@@ -69,7 +68,7 @@ hipError_t launch_attn_f32(AttnMode mode, int D, const AttnArgs& a, hipStream_t 
 hipError_t launch_select(bool bf16, int D, const SelectArgs& a, hipStream_t s);
 
 // Scratch of the allocation-free selector: a static device array of this many
-// bytes (select.hip) holding the pooled means.  select_scratch returns its
+// bytes (select.hip) holding the K means.  select_scratch returns its
 // address on the current device, looked up once per device.
 constexpr size_t kSelectScratchBytes = size_t(16) << 20;
 hipError_t select_scratch(void** ptr);

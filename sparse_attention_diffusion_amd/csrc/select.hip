@@ -8,19 +8,14 @@
 // plus the best remaining ones (ties to the lower block index).
 //
 // Kernels
-//   pool_kernel   : one wave per (tensor, bh, block).  The block's rows are
-//                   read as 16-byte chunks, all at once (HBM-bound: Q and K
-//                   are read once); float32 partial sums per row group are
-//                   reduced through LDS.  K means are written transposed
-//                   ([bh][d][block]) so that scoring reads them coalesced.
-//   select_kernel : one wave per (bh, QG = 8 query blocks; 4 above 512 key
-//                   blocks).  Lane j scores key
-//                   blocks j, j+64, ... against the QG pooled queries (float32
-//                   dot products in ascending d), then each query block's
-//                   keep - n_forced winners are taken by rounds of a wave-wide
-//                   maximum of 64-bit (score, ~index) keys, and the list is
-//                   written in ascending order through a flag row and ballots.
-//                   Large selections fall back to a bitonic sort in LDS.
+//   pool_k_kernel : one wave per (bh, key block) mean of K, HBM-bound (K read
+//                   once), written transposed ([bh][d][block]).
+//   select_kernel : pools its own query blocks straight from Q (no round trip
+//                   of the query means through memory), scores them against
+//                   the K means staged 64 blocks at a time in LDS, and takes
+//                   each query block's kept list: forced blocks plus the
+//                   keep - n_forced best others (rounds of a wave-wide maximum
+//                   of 64-bit keys; a bitonic sort in LDS above 32 winners).
 #include <mutex>
 #include <vector>
 
@@ -81,9 +76,12 @@ struct Chunk<__bf16> {
   }
 };
 
-// grid.x: (bh, block) pairs laid out per XCD; grid.y: 0 = q, 1 = k.
+// Mean of every key block, written transposed ([bh][d][block]) so that the
+// selecting kernel reads a chunk of 64 blocks' means per d contiguously.
+// One wave per (bh, block): the block's rows are read as 16-byte chunks, all
+// at once; float32 partial sums per row group are reduced through LDS.
 template <typename T, int D>
-__global__ void __launch_bounds__(64) pool_kernel(SelectArgs a, XcdGrid grid) {
+__global__ void __launch_bounds__(64) pool_k_kernel(SelectArgs a, XcdGrid grid) {
   constexpr int E = Chunk<T>::E;          // elements per 16-byte chunk
   constexpr int CPR = D / E;              // chunks per row
   constexpr int RPI = 64 / CPR;           // rows per pass of the wave
@@ -95,11 +93,10 @@ __global__ void __launch_bounds__(64) pool_kernel(SelectArgs a, XcdGrid grid) {
   if (lin >= grid.total) return;
   const int Nb = a.Nb, N = a.N;
   const int bh = lin / Nb, i = lin % Nb;
-  const bool isk = blockIdx.y != 0;
   const int lane = threadIdx.x;
   const int rg = lane / CPR, ch = lane % CPR;  // row in the pass, chunk in the row
   const int r0 = i * kBlock, rows = min(N - r0, kBlock);
-  const char* base = (const char*)((const T*)(isk ? a.k : a.q) + ((size_t)bh * N + r0) * D);
+  const char* base = (const char*)((const T*)a.k + ((size_t)bh * N + r0) * D);
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
@@ -127,8 +124,7 @@ __global__ void __launch_bounds__(64) pool_kernel(SelectArgs a, XcdGrid grid) {
     float s = 0.f;
 #pragma unroll
     for (int g = 0; g < RPI; ++g) s += part[g][d];
-    if (isk) a.kb[((size_t)bh * D + d) * Nb + i] = s * inv;  // transposed
-    else a.qb[((size_t)bh * Nb + i) * D + d] = s * inv;
+    a.kb[((size_t)bh * D + d) * Nb + i] = s * inv;
   }
 }
 
@@ -138,41 +134,80 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// 64-bit value of another lane of the same row of 16, by DPP control C.
+template <int C>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long x) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)x, C, 0xF, 0xF, false);
+  const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(x >> 32), C, 0xF, 0xF, false);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Maximum over the wave, returned in every lane (uniform).  Within each row of
+// 16 lanes: DPP quad permutations (lane ^ 1, lane ^ 2), then the half-row and
+// row mirrors; the four row maxima are then read into scalar registers.
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x) {
+  unsigned long long y;
+  y = dpp_u64<0xB1>(x);   // quad_perm [1,0,3,2]
+  x = y > x ? y : x;
+  y = dpp_u64<0x4E>(x);   // quad_perm [2,3,0,1]
+  x = y > x ? y : x;
+  y = dpp_u64<0x141>(x);  // row_half_mirror
+  x = y > x ? y : x;
+  y = dpp_u64<0x140>(x);  // row_mirror
+  x = y > x ? y : x;
+  unsigned long long m = 0ull;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const unsigned lo = __shfl_xor((unsigned)x, o), hi = __shfl_xor((unsigned)(x >> 32), o);
-    const unsigned long long y = ((unsigned long long)hi << 32) | lo;
-    x = y > x ? y : x;
+  for (int r = 0; r < 4; ++r) {
+    const unsigned lo = __builtin_amdgcn_readlane((unsigned)x, 16 * r);
+    const unsigned hi = __builtin_amdgcn_readlane((unsigned)(x >> 32), 16 * r);
+    const unsigned long long v = ((unsigned long long)hi << 32) | lo;
+    m = v > m ? v : m;
   }
-  return x;
+  return m;
+}
+
+// Orders this wave's LDS accesses: one wave's LDS instructions execute in
+// order, so every lane's earlier LDS writes are seen by later reads of any
+// lane once the compiler keeps them in program order; this is that compiler
+// barrier.  (A memory fence would also wait for the wave's global stores.)
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
 }
 
 constexpr int kMaxRounds = 32;  // above this many non-forced winners: bitonic sort
+constexpr int kMaxSelLds = 64 << 10;  // dynamic LDS of one selecting workgroup at most
 
-// Query blocks per wave: 8 while the per-lane scores fit in registers.
+// Query blocks per wave: 4 (2 above 512 key blocks, where the per-lane
+// scores take more registers), so that many waves share each SIMD.
 template <int CH>
-constexpr int query_group() { return CH <= 8 ? 8 : 4; }
+constexpr int query_group() { return CH <= 8 ? 4 : 2; }
 
-// Dynamic LDS of select_kernel: pooled queries [QG][D] floats, flag rows
-// [QG][Nb rounded up to 4] bytes, and (bitonic fallback only) P 64-bit keys.
+// Dynamic LDS of select_kernel: a chunk of 64 blocks' K means [D][64]
+// floats shared by the workgroup, then per wave: pooled queries [QG][D],
+// pooling partials [RPI][D] (floats), one flag row (Nb rounded up to 16
+// bytes) and, for the bitonic fallback only, P 64-bit keys.
 struct SelectLds {
-  int flag_stride, keys_off, bytes;
+  int kc_bytes, wave_bytes, q_off, part_off, flag_off, flag_stride, keys_off, bytes;
 };
-inline SelectLds select_lds(int QG, int D, int Nb, bool bitonic) {
+inline SelectLds select_lds(int W, int QG, int D, int RPI, int Nb, bool bitonic) {
   SelectLds l;
-  l.flag_stride = (Nb + 3) & ~3;
-  const int flags_off = QG * D * 4;
-  l.keys_off = (flags_off + QG * l.flag_stride + 7) & ~7;
+  l.kc_bytes = D * 64 * 4;
+  l.q_off = 0;
+  l.part_off = QG * D * 4;
+  l.flag_off = l.part_off + RPI * D * 4;
+  l.flag_stride = (Nb + 15) & ~15;
+  l.keys_off = (l.flag_off + l.flag_stride + 7) & ~7;
   int P = 64;
   while (P < Nb) P <<= 1;
-  l.bytes = l.keys_off + (bitonic ? P * 8 : 0);
+  l.wave_bytes = (l.keys_off + (bitonic ? P * 8 : 0) + 15) & ~15;
+  l.bytes = l.kc_bytes + W * l.wave_bytes;
   return l;
 }
 
 // Writes the kept list of one query block from its flag row (ascending).
 __device__ __forceinline__ void emit(const unsigned char* flags, int Nb, int32_t* out) {
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   int cnt = 0;
   for (int base = 0; base < Nb; base += 64) {
     const int j = base + lane;
@@ -183,69 +218,151 @@ __device__ __forceinline__ void emit(const unsigned char* flags, int Nb, int32_t
   }
 }
 
-// CH: key blocks per lane (64-block chunks), at least ceil(Nb / 64).
-template <int D, int CH>
-__global__ void __launch_bounds__(64) select_kernel(SelectArgs a, XcdGrid grid, SelectLds lay) {
+// The selecting kernel: pools its query blocks straight from q, scores them
+// against the K means and takes each one's kept list.  One workgroup of
+// W waves (4, or 2 where four would need more than 64 KB of LDS) per
+// (bh, W * QG query blocks); wave w owns QG consecutive query blocks.
+//   1. pooling: the rows of each of the wave's query blocks are read as
+//      16-byte chunks, all at once, summed in float32 per row group and
+//      reduced through the wave's LDS (then multiplied by 1/rows);
+//   2. scores: the workgroup stages the K means of 64 key blocks at a time in
+//      LDS; lane j of every wave scores key block 64c + j against the wave's
+//      pooled queries (float32 products summed in ascending d);
+//   3. per query block: forced blocks are flagged, the keep - n_forced
+//      winners by (score desc, index asc) are taken by rounds of a wave-wide
+//      maximum of 64-bit (score bits, ~index) keys (a bitonic sort in the
+//      wave's LDS above 32 winners), and the list is written ascending from
+//      the flag row with ballots.
+// Only the staging of the K means synchronises the workgroup; everything
+// else is wave-local, so waves with fewer (or no) query blocks never hold
+// the others at a barrier.
+template <typename T, int D, int CH, int W>
+__global__ void __launch_bounds__(64 * W) select_kernel(SelectArgs a, XcdGrid grid, SelectLds lay) {
   constexpr int QG = query_group<CH>();
+  constexpr int E = Chunk<T>::E, CPR = D / E, RPI = 64 / CPR, PASSES = (kBlock + RPI - 1) / RPI;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  float(*qrow)[D] = (float(*)[D])smem;
-  unsigned char* flag0 = (unsigned char*)smem + QG * D * 4;
-  unsigned long long* keys = (unsigned long long*)(smem + lay.keys_off);
+  float(*kc)[64] = (float(*)[64])smem;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  char* wb = smem + lay.kc_bytes + wave * lay.wave_bytes;
+  float(*qrow)[D] = (float(*)[D])(wb + lay.q_off);
+  float(*part)[D] = (float(*)[D])(wb + lay.part_off);
+  unsigned char* flags = (unsigned char*)(wb + lay.flag_off);
+  unsigned long long* keys = (unsigned long long*)(wb + lay.keys_off);
 
   const uint32_t lin = grid.linear(blockIdx.x);
-  if (lin >= grid.total) return;
-  const int Nb = a.Nb, keep = a.keep;
-  const int groups = (Nb + QG - 1) / QG;
-  const int bh = lin / groups, i0 = (lin % groups) * QG;
-  const int nq = min(QG, Nb - i0);
-  const int lane = threadIdx.x;
-  for (int e = lane; e < QG * D; e += 64) {
-    const int g = e / D, d = e % D;
-    qrow[g][d] = g < nq ? a.qb[((size_t)bh * Nb + i0 + g) * D + d] : 0.f;
+  if (lin >= grid.total) return;  // the whole workgroup
+  const int Nb = a.Nb, N = a.N, keep = a.keep;
+  constexpr int QW = W * QG;
+  const int groups = (Nb + QW - 1) / QW;
+  const int bh = lin / groups;
+  const int i0 = (lin % groups) * QW + wave * QG;  // this wave's first query block
+  const int nq = max(0, min(QG, Nb - i0));
+
+  // 1. pooled queries; the rows of block g + 1 are in flight while block g is
+  // reduced.  A buffer resource per block zero-fills rows past N (branch-free).
+  const int rg = lane / CPR, ch = lane % CPR;
+  const int rgl = min(rg, RPI - 1);  // lanes past the last row group load a duplicate, unused
+  u32x4 buf[2][PASSES];
+  auto issue_rows = [&](u32x4 (&c)[PASSES], int g) {
+    const int r0 = (i0 + g) * kBlock, rows = min(N - r0, kBlock);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>((const T*)a.q + ((size_t)bh * N + r0) * D), (short)0, rows * D * (int)sizeof(T), 0x00020000);
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+      c[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rs, ((p * RPI + rgl) * D + ch * E) * (int)sizeof(T), 0, 0));
+  };
+  if (nq > 0) issue_rows(buf[0], 0);
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    if (g < nq) {
+      const int rows = min(N - (i0 + g) * kBlock, kBlock);
+      if (g + 1 < nq) issue_rows(buf[(g + 1) & 1], g + 1);
+      if (rg < RPI) {
+        float acc[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = 0.f;
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+          float f[8];
+          Chunk<T>::widen(buf[g & 1][p], f);
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[e] += f[e];
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) part[rg][ch * E + e] = acc[e];
+      }
+      wave_sync();
+      const float inv = 1.f / (float)rows;
+      for (int d = lane; d < D; d += 64) {
+        float sum = 0.f;
+#pragma unroll
+        for (int r = 0; r < RPI; ++r) sum += part[r][d];
+        qrow[g][d] = sum * inv;
+      }
+      wave_sync();
+    } else {
+      for (int d = lane; d < D; d += 64) qrow[g][d] = 0.f;  // unused; keeps the scores finite
+    }
   }
-  for (int e = lane; e < QG * lay.flag_stride / 4; e += 64) ((uint32_t*)flag0)[e] = 0u;
+  for (int e = lane; e < lay.flag_stride / 4; e += 64) ((uint32_t*)flags)[e] = 0u;
   int n_forced = 0;
 #pragma unroll
   for (int w = 0; w < kMaxBlocks / 32; ++w) n_forced += __popc(a.forced[w]);
-  __syncthreads();
+  wave_sync();
 
-  // Scores of key blocks j = lane + 64c against the QG pooled queries: float32
-  // products summed in ascending d; the K means of 16 d at a time are loaded
-  // together.
+  // 2. scores of key blocks j = 64c + lane against the wave's pooled queries
+  // The next chunk's means are loaded into registers while this one is scored.
   const float* kt = a.kb + (size_t)bh * D * Nb;  // transposed means [d][j]
   const int nc = (Nb + 63) / 64;
+  constexpr int PER = D / W;  // means per thread and chunk
+  float nxt[PER];
+  auto load_chunk = [&](int c) {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int e = (int)threadIdx.x + r * 64 * W;
+      nxt[r] = kt[(size_t)(e >> 6) * Nb + min(c * 64 + (e & 63), Nb - 1)];
+    }
+  };
+  load_chunk(0);
   float sc[QG][CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    if (c < nc) {
-      const int jj = min(c * 64 + lane, Nb - 1);
+    if (c < nc) {  // the same for the whole workgroup
+      __syncthreads();  // the previous chunk is consumed
+#pragma unroll
+      for (int r = 0; r < PER; ++r) {
+        const int e = (int)threadIdx.x + r * 64 * W;
+        kc[e >> 6][e & 63] = nxt[r];
+      }
+      __syncthreads();
+      if (c + 1 < nc) load_chunk(c + 1);
       float acc[QG];
 #pragma unroll
       for (int g = 0; g < QG; ++g) acc[g] = 0.f;
 #pragma unroll
-      for (int d0 = 0; d0 < D; d0 += 16) {
-        float kv[16];
+      for (int d0 = 0; d0 < D; d0 += 4) {
+        float kv[4];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) kv[e] = kt[(size_t)(d0 + e) * Nb + jj];
+        for (int e = 0; e < 4; ++e) kv[e] = kc[d0 + e][lane];
 #pragma unroll
-        for (int e4 = 0; e4 < 16; e4 += 4)
+        for (int g = 0; g < QG; ++g) {
+          const f32x4 qv = *(const f32x4*)&qrow[g][d0];
 #pragma unroll
-          for (int g = 0; g < QG; ++g) {
-            const f32x4 qv = *(const f32x4*)&qrow[g][d0 + e4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[g] = fmaf(qv[e], kv[e4 + e], acc[g]);
-          }
+          for (int e = 0; e < 4; ++e) acc[g] = fmaf(qv[e], kv[e], acc[g]);
+        }
       }
 #pragma unroll
       for (int g = 0; g < QG; ++g) sc[g][c] = acc[g] * a.alpha + 0.0f;  // + 0: -0 -> +0
     }
   }
 
+  // 3. the kept list of each of the wave's query blocks
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
     if (g >= nq) break;
     const int i = i0 + g;
-    unsigned char* flags = flag0 + g * lay.flag_stride;
     if (a.scores) {
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
@@ -282,7 +399,7 @@ __global__ void __launch_bounds__(64) select_kernel(SelectArgs a, XcdGrid grid, 
         }
       }
     } else {
-      // Bitonic sort of the non-forced keys, descending.
+      // Bitonic sort of the non-forced keys, descending, in this wave's LDS.
       int P = 64;
       while (P < Nb) P <<= 1;
 #pragma unroll
@@ -291,7 +408,7 @@ __global__ void __launch_bounds__(64) select_kernel(SelectArgs a, XcdGrid grid, 
       // P can exceed the CH*64 keys this lane holds (CH = 5 sorts 512 keys):
       // the rest of the sort buffer is padding and must lose every compare.
       for (int t = CH * 64 + lane; t < P; t += 64) keys[t] = 0ull;
-      __syncthreads();
+      wave_sync();
       for (int k = 2; k <= P; k <<= 1) {
         for (int jx = k >> 1; jx > 0; jx >>= 1) {
           for (int t = lane; t < (P >> 1); t += 64) {
@@ -304,7 +421,7 @@ __global__ void __launch_bounds__(64) select_kernel(SelectArgs a, XcdGrid grid, 
               keys[hi] = x;
             }
           }
-          __syncthreads();
+          wave_sync();
         }
       }
       // rounds <= Nb - n_forced candidates, so the first `rounds` keys are real;
@@ -312,34 +429,45 @@ __global__ void __launch_bounds__(64) select_kernel(SelectArgs a, XcdGrid grid, 
       for (int t = lane; t < rounds; t += 64)
         if (keys[t] != 0ull) flags[0xFFFFFFFFu - (uint32_t)(keys[t] & 0xFFFFFFFFull)] = 1;
     }
-    __syncthreads();
+    wave_sync();
     emit(flags, Nb, a.idx + ((size_t)bh * Nb + i) * keep);
+    wave_sync();
+    for (int e = lane; e < lay.flag_stride / 4; e += 64) ((uint32_t*)flags)[e] = 0u;  // for the next block
+    wave_sync();
   }
 }
 
-template <int D, int CH>
+template <typename T, int D, int CH>
 void launch_select_ch(const SelectArgs& a, hipStream_t s) {
   constexpr int QG = query_group<CH>();
+  constexpr int RPI = 64 / (D / Chunk<T>::E);
   int n_forced = 0;
   for (int w = 0; w < kMaxBlocks / 32; ++w) n_forced += __builtin_popcount(a.forced[w]);
-  const SelectLds lay = select_lds(QG, D, a.Nb, a.keep - n_forced > kMaxRounds);
-  XcdGrid sg = make_xcd_grid((uint32_t)a.BH * (uint32_t)((a.Nb + QG - 1) / QG));
-  hipLaunchKernelGGL((select_kernel<D, CH>), dim3(sg.grid()), dim3(64), lay.bytes, s, a, sg, lay);
+  const bool bitonic = a.keep - n_forced > kMaxRounds;
+  const SelectLds l4 = select_lds(4, QG, D, RPI, a.Nb, bitonic);
+  if (l4.bytes <= kMaxSelLds) {
+    XcdGrid sg = make_xcd_grid((uint32_t)a.BH * (uint32_t)((a.Nb + 4 * QG - 1) / (4 * QG)));
+    hipLaunchKernelGGL((select_kernel<T, D, CH, 4>), dim3(sg.grid()), dim3(256), l4.bytes, s, a, sg, l4);
+  } else {
+    const SelectLds l2 = select_lds(2, QG, D, RPI, a.Nb, bitonic);
+    XcdGrid sg = make_xcd_grid((uint32_t)a.BH * (uint32_t)((a.Nb + 2 * QG - 1) / (2 * QG)));
+    hipLaunchKernelGGL((select_kernel<T, D, CH, 2>), dim3(sg.grid()), dim3(128), l2.bytes, s, a, sg, l2);
+  }
 }
 
 template <typename T, int D>
 hipError_t launch_typed(const SelectArgs& a, hipStream_t s) {
   XcdGrid pg = make_xcd_grid((uint32_t)a.BH * (uint32_t)a.Nb);
-  hipLaunchKernelGGL((pool_kernel<T, D>), dim3(pg.grid(), 2), dim3(64), 0, s, a, pg);
+  hipLaunchKernelGGL((pool_k_kernel<T, D>), dim3(pg.grid()), dim3(64), 0, s, a, pg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nc = (a.Nb + 63) / 64;
-  if (nc <= 1) launch_select_ch<D, 1>(a, s);
-  else if (nc <= 2) launch_select_ch<D, 2>(a, s);
-  else if (nc <= 4) launch_select_ch<D, 4>(a, s);
-  else if (nc <= 5) launch_select_ch<D, 5>(a, s);
-  else if (nc <= 8) launch_select_ch<D, 8>(a, s);
-  else launch_select_ch<D, kMaxBlocks / 64>(a, s);
+  if (nc <= 1) launch_select_ch<T, D, 1>(a, s);
+  else if (nc <= 2) launch_select_ch<T, D, 2>(a, s);
+  else if (nc <= 4) launch_select_ch<T, D, 4>(a, s);
+  else if (nc <= 5) launch_select_ch<T, D, 5>(a, s);
+  else if (nc <= 8) launch_select_ch<T, D, 8>(a, s);
+  else launch_select_ch<T, D, kMaxBlocks / 64>(a, s);
   return hipGetLastError();
 }
 
