@@ -35,7 +35,9 @@ SHORT = [("sparse_occ_kernel<64, false, false>", "sparse reshape R1 (d_pad 64)")
          ("calib_kernel<64, 2, 2, true>", "calibration, bf16 residual (d_pad 64)"),
          ("calib_kernel<80, 2, 2, true>", "calibration, bf16 residual (d_pad 80)"),
          ("calib_kernel<64", "calibration (d_pad 64)"), ("calib_kernel<80", "calibration (d_pad 80)"),
-         ("attn_f32_kernel", "float32 attention"), ("select_kernel", "block top-k"), ("pool_kernel", "block pooling")]
+         ("attn_f32_kernel", "float32 attention"),
+         ("select_kernel", "selector: query pooling, scores, top-k"), ("pool_k_kernel", "selector: key pooling"),
+         ("permute_kernel", "row reorder")]
 
 
 def short_name(name):

@@ -74,8 +74,8 @@ def test_profile_summary_from_csv(tmp_path):
     assert abs(per["sparse reshape R1 (d_pad 64)"] - 600000.0 * 1024 * 2) < 1e-3
     # every kernel of the library has a label, and the bf16/R2 variants are not merged with R1
     names = ["sparse_occ_kernel<64, true, false>", "sparse_occ_kernel<64, false, true>",
-             "sparse_occ_kernel<80, true, true>", "calib_kernel<80, 2, 2, true>", "pool_kernel<__bf16, 64>",
-             "select_kernel<64, 5>", "attn_f32_kernel<64, 1>"]
+             "sparse_occ_kernel<80, true, true>", "calib_kernel<80, 2, 2, true>", "pool_k_kernel<__bf16, 64>",
+             "select_kernel<__bf16, 64, 5, 4>", "attn_f32_kernel<64, 1>", "permute_kernel"]
     labels = [profsum.short_name(n) for n in names]
     assert None not in labels and len(set(labels)) == len(labels)
 
