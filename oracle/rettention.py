@@ -8,9 +8,10 @@ Generation via Attention Statistical Reshape").
 
 * Teaser paragraph: statistics cached across denoising steps reshape sparse
   attention so that the full attention distribution is recovered.
-* Abstract: sparse attention keeps a subset of tokens (as few as 3.1%); the
-  reshape uses the softmax distribution history to undo the normalisation
-  shift that renormalising over a subset causes.
+* Abstract: sparse attention attends to a small fraction of the tokens (the
+  page reports 3.1%); renormalising the softmax over that fraction shifts the
+  probabilities, and the reshape corrects the shift with the softmax statistics
+  of earlier steps.
 * Core-mechanism paragraph: the ratio of sparse to full softmax denominators is
   reused, and the contribution of masked-out tokens is cached as a residual.
 

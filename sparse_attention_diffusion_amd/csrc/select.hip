@@ -1,8 +1,8 @@
 // Block selector: mean-pooled Q/K per 64-token block, pooled logits, and a
 // per-query-block top-k with always-kept (forced) blocks.
 //
-// Method: the Re-ttention project page keeps just a few of the tokens
-// (Abstract: as few as 3.1%).  How the subset is chosen is not spelled out
+// Method: the Re-ttention project page keeps a small fraction of the tokens
+// (Abstract: 3.1% in its experiments).  How the subset is chosen is not spelled out
 // there; this library scores 64-token blocks by the scaled dot product of
 // their mean query and mean key and keeps, per query block, the forced blocks
 // plus the best remaining ones (ties to the lower block index).
