@@ -658,8 +658,9 @@ template <int D, bool RB, bool V2>
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 3, 4)))
 sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
   constexpr int NT = Shape<D>::NT, KS = Shape<D>::KS, TILE = Shape<D>::TILE, ROW = Shape<D>::ROW;
-  constexpr int NST = D / 8;          // O stores (and residual loads) per lane
-  constexpr int NLD = V2 ? KS + 2 : KS + NST + 3;  // per-query-block loads (Q, statistics, R1: residual)
+  constexpr int NST = D / 16;         // O stores per lane (whole lines, staged through LDS)
+  constexpr int NRL = D / 8;          // residual loads per lane
+  constexpr int NLD = V2 ? KS + 2 : KS + NRL + 3;  // per-query-block loads (Q, statistics, R1: residual)
   __shared__ __attribute__((aligned(1024))) char ring[2 * TILE];  // K slot, V slot
   char* const kslot = ring;
   char* const vslot = ring + TILE;
@@ -815,6 +816,23 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
       }
       const size_t r0 = (size_t)it.bh * N + (size_t)it.qi * kBlock;
       const __amdgpu_buffer_rsrc_t ro = make_rsrc((const char*)a.o + r0 * D * 2, min(N - it.qi * kBlock, kBlock) * D * 2);
+      // The output goes through the V slot (free once both waves are past
+      // their last P.V): each wave writes its 32 rows there in the MFMA
+      // layout, reads them back row-contiguous and stores whole 128-byte
+      // lines, instead of 16 bytes of 32 different lines per store
+      // instruction.  d = 64 rows (128 bytes) have their 16-byte units
+      // XOR-swizzled by row & 7 against bank conflicts on the writes; the
+      // 160-byte rows of d = 80 spread over the banks as they are.
+      constexpr int RBYTES = D * 2;
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's V reads are done
+      __builtin_amdgcn_s_barrier();
+      char* const stage = vslot + wave * 32 * RBYTES;
+      // Offsets are made opaque per query block so that the compiler keeps
+      // one register for them rather than hoisting every derived address
+      // out of the loop.
+      uint32_t woff = D == 64 ? l32 * 128 + (l32 & 7) * 16 : l32 * RBYTES;
+      uint32_t roff = D == 64 ? (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) * 16) : lane * 16;
+      asm volatile("" : "+v"(woff), "+v"(roff));
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -824,8 +842,19 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               ob[e] = V2 ? (__bf16)fmaf(o[t][4 * i4 + e], w, rv[t][i4][e] * u) : (__bf16)(o[t][4 * i4 + e] * w);
-            __builtin_amdgcn_raw_buffer_store_b64(*(u32x2*)ob, ro, (rowq * D + 32 * t + 8 * i4 + 4 * g) * 2, 0, 0);
+            const uint32_t unit = 4 * t + i4;
+            const uint32_t at = D == 64 ? (woff ^ (unit * 16)) : woff + unit * 16;
+            *(u32x2*)(stage + at + 8 * g) = *(u32x2*)ob;
           }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      // 16-byte unit c*64 + lane of the wave's 32 rows, row-major: the same
+      // linear offset in the output.
+#pragma unroll
+      for (int cc = 0; cc < 32 * RBYTES / 1024; ++cc) {
+        const u32x4 v = *(const u32x4*)(stage + roff + cc * 1024);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ro, wave * 32 * RBYTES + (int)lane * 16 + cc * 1024, 0, 0);
+      }
     }
     if (k + 1 < n_items) {
       it = nit;
