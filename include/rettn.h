@@ -102,12 +102,12 @@ typedef struct rt_stats_cache rt_stats_cache;
 
 /* Device pointers of one layer of the statistics cache.
  *   m, z_full, z_sparse : float32 [B, H, N]
- *   R                   : [B, H, N, d_pad], row-major; float32 by default, bf16
- *                         (reinterpret the pointer) when r_dtype == RT_BF16
+ *   R                   : B*H*Nb*64*d_pad elements, float32 by default, bf16
+ *                         (reinterpret the pointer) when r_dtype == RT_BF16, in
+ *                         the order rt_residual_index gives (not row-major)
  *   idx                 : int32   [B, H, Nb, keep], the kept list used at calibration
  * (Differs from a plain pointer struct in two fields: `rows` = B*H*N gives the
- * extent of the row-wise arrays, and `r_dtype` says how R is stored; the row
- * stride of R is always d_pad elements.)
+ * extent of the row-wise arrays, and `r_dtype` says how R is stored.)
  * `valid` is 1 once the layer has been calibrated (or marked valid).       */
 typedef struct {
   float* m;
@@ -185,6 +185,16 @@ size_t rt_stats_cache_bytes_ex(const rt_shape* shape, int32_t n_layers, int32_t 
 rt_status rt_stats_cache_init_ex(rt_stats_cache** out, const rt_shape* shape, int32_t n_layers,
                                  int32_t residual_dtype, void* dev_mem, size_t bytes);
 rt_status rt_stats_cache_view(const rt_stats_cache* cache, int32_t layer, rt_stats_view* out);
+/* Position, in elements from rt_stats_view.R, of the residual of head
+ * bh = b*H + h, row `row` (< N), column `col` (< d_pad).  R is stored in
+ * blocks of 64 rows, the last one padded past N (padding rows hold
+ * unspecified finite values, or anything after a restore, and never enter a
+ * result).  Inside a block the element of row r and column c sits at
+ *   ((r/32 * d_pad/8 + c/8) * 64 + 32 * (c/4 % 2) + r % 32) * 4 + c % 4,
+ * the order in which the attention kernels' matrix-core accumulators hold a
+ * block, so that they load and store it in contiguous runs.  Returns -1 for
+ * an invalid shape or an element out of range (rt_last_error says which). */
+int64_t rt_residual_index(const rt_shape* shape, int64_t bh, int32_t row, int32_t col);
 rt_status rt_stats_cache_set_valid(rt_stats_cache* cache, int32_t layer, int32_t valid);
 rt_status rt_stats_cache_invalidate(rt_stats_cache* cache, int32_t layer);
 rt_status rt_stats_cache_destroy(rt_stats_cache* cache);

@@ -120,7 +120,9 @@ void layout(rt_stats_cache* c) {
   c->off_m = off; off += align_up(rows * 4);
   c->off_zf = off; off += align_up(rows * 4);
   c->off_zs = off; off += align_up(rows * 4);
-  c->off_R = off; off += align_up(rows * s.d_pad * (c->r_dtype == RT_BF16 ? 2 : 4));
+  // R is padded to whole 64-row blocks (rettn::residual_index)
+  const size_t r_elems = (size_t)s.B * s.H * nblocks(s.N) * rettn::kBlock * s.d_pad;
+  c->off_R = off; off += align_up(r_elems * (c->r_dtype == RT_BF16 ? 2 : 4));
   c->off_idx = off; off += align_up(lists * 4);
   c->layer_stride = off;
 }
@@ -295,6 +297,15 @@ size_t rt_stats_cache_bytes_ex(const rt_shape* s, int32_t n_layers, int32_t resi
   c.r_dtype = residual_dtype;
   layout(&c);
   return c.layer_stride * (size_t)n_layers;
+}
+
+int64_t rt_residual_index(const rt_shape* s, int64_t bh, int32_t row, int32_t col) {
+  if (s == nullptr || check_shape(s) != RT_OK) return -1;
+  if (bh < 0 || bh >= (int64_t)s->B * s->H || row < 0 || row >= s->N || col < 0 || col >= s->d_pad) {
+    fail(RT_E_ARG, "residual element (bh=%lld, row=%d, col=%d) out of range", (long long)bh, row, col);
+    return -1;
+  }
+  return (int64_t)rettn::residual_index((size_t)bh, (int)nblocks(s->N), s->d_pad, row, col);
 }
 
 size_t rt_stats_cache_bytes(const rt_shape* s, int32_t n_layers) {

@@ -584,28 +584,33 @@ __device__ __forceinline__ void load_qs(bf16x8 (&q)[Shape<D>::KS], PipeStats<D>&
                              __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.z_sparse + r0, rows * 4), rowq * 4, 0, 0));
 }
 
-// Cached residual of one query block in accumulator order: D/8 loads.
+// Cached residual of one query block in accumulator order: D/8 loads.  The
+// cache holds it in that order (residual_index), padded to 64 rows, so every
+// load is one contiguous run over the wave's lanes.
 template <int D, bool RB>
 __device__ __forceinline__ void load_residual(f32x4 (&r)[Shape<D>::NT][4], const AttnArgs& a, int bh, int qi, int rowq,
                                               int g) {
-  const size_t r0 = (size_t)bh * a.N + (size_t)qi * kBlock;
-  const int rows = min(a.N - qi * kBlock, kBlock);
+  // The wave's 32 rows: D/8 runs of 256 elements from this base.
+  const size_t r0 = ((size_t)bh * a.Nb + (size_t)qi) * kBlock * D + (size_t)(rowq >> 5) * 32 * D;
   const __amdgpu_buffer_rsrc_t rr =
-      RB ? make_rsrc((const __bf16*)a.R + r0 * D, rows * D * 2) : make_rsrc(a.R + r0 * D, rows * D * 4);
+      RB ? make_rsrc((const __bf16*)a.R + r0, 32 * D * 2) : make_rsrc(a.R + r0, 32 * D * 4);
+  // This lane's bytes into each run; kept opaque so that the compiler adds
+  // the run offsets as constants instead of holding one register per run.
+  int lo = (32 * g + (rowq & 31)) * 4 * (RB ? 2 : 4);
+  asm volatile("" : "+v"(lo));
 #pragma unroll
   for (int t = 0; t < Shape<D>::NT; ++t)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
+      const int run = (4 * t + i4) * 256 * (RB ? 2 : 4);  // bytes before this run
       if (32 * t + 8 * i4 >= D) {
         r[t][i4] = f32x4{};
       } else if (RB) {  // four bf16, widened exactly
-        const u32x2 h = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rr, (rowq * D + 32 * t + 8 * i4 + 4 * g) * 2, 0, 0));
+        const u32x2 h = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rr, lo + run, 0, 0));
         r[t][i4] = f32x4{__uint_as_float(h[0] << 16), __uint_as_float(h[0] & 0xFFFF0000u),
                          __uint_as_float(h[1] << 16), __uint_as_float(h[1] & 0xFFFF0000u)};
       } else {
-        r[t][i4] = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, (rowq * D + 32 * t + 8 * i4 + 4 * g) * 4, 0, 0));
+        r[t][i4] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, lo + run, 0, 0));
       }
     }
 }
@@ -1007,21 +1012,27 @@ calib_kernel(AttnArgs a, XcdGrid grid) {
   const float f = __builtin_amdgcn_exp2f((cx.st.m_ref - cx.st.m_true) * cx.c);
   const float zs = pair_sum(cx.zk) * f;
   const float zf = pair_sum(cx.zall) * f;
-  if (row_ok) {
-    const size_t srow = (size_t)bh * N + row;
-    if (g == 0) {
-      a.m[srow] = cx.st.m_true * a.alpha;
-      a.z_full[srow] = zf;
-      a.z_sparse[srow] = zs;
-    }
+  const size_t srow = (size_t)bh * N + row;
+  if (row_ok && g == 0) {
+    a.m[srow] = cx.st.m_true * a.alpha;
+    a.z_full[srow] = zf;
+    a.z_sparse[srow] = zs;
+  }
+  // The residual goes out for every row of the block, the padding rows past N
+  // included (they repeat query row N-1, so the values are finite), in
+  // the cache's accumulator order: each store is one run over the wave's
+  // lanes.  O only for the rows that exist.
+  if (qi < Nb) {
     const float inv = 1.f / zf;
     __bf16* orow = (__bf16*)a.o + srow * D;
+    const size_t rblock = ((size_t)bh * Nb + qi) * kBlock * D;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int d = 32 * t + 8 * i4 + 4 * g;
         if (d < D) {
+          const size_t at = rblock + (size_t)(((wave & 1) * (D / 8) + 4 * t + i4) * 64 + lane) * 4;
           f32x4 r;
           __bf16 ob[4];
 #pragma unroll
@@ -1033,11 +1044,11 @@ calib_kernel(AttnArgs a, XcdGrid grid) {
             __bf16 rb[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) rb[e] = (__bf16)r[e];
-            *(u32x2*)((__bf16*)a.R + srow * D + d) = *(u32x2*)rb;
+            *(u32x2*)((__bf16*)a.R + at) = *(u32x2*)rb;
           } else {
-            *(f32x4*)(a.R + srow * D + d) = r;
+            *(f32x4*)(a.R + at) = r;
           }
-          *(u32x2*)(orow + d) = *(u32x2*)ob;
+          if (row_ok) *(u32x2*)(orow + d) = *(u32x2*)ob;
         }
       }
   }

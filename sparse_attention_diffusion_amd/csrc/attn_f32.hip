@@ -129,26 +129,23 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnArgs a, XcdGrid 
     a.m[srow] = m;
     a.z_full[srow] = zf;
     a.z_sparse[srow] = zs;
-    float* rrow = a.R + srow * D;
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      rrow[d] = o[d];
+      a.R[residual_index(bh, a.Nb, D, row, d)] = o[d];
       orow[d] = (ok[d] * corr + o[d]) / zf;
     }
   } else if (a.variant == 1) {  // R2: r * O_sparse + R / Z_full
     const float zf_c = a.z_full[srow], zs_c = a.z_sparse[srow];
     const float w = zs_c / (zf_c * z);
-    const float* rrow = a.R + srow * D;
 #pragma unroll
-    for (int d = 0; d < D; ++d) orow[d] = fmaf(o[d], w, rrow[d] / zf_c);
+    for (int d = 0; d < D; ++d) orow[d] = fmaf(o[d], w, a.R[residual_index(bh, a.Nb, D, row, d)] / zf_c);
   } else {
     const float m_c = a.m[srow], zf_c = a.z_full[srow], zs_c = a.z_sparse[srow];
     const float big = fmaxf(m, m_c);
     const float e1 = expf(m - big), e2 = expf(m_c - big);
     const float den = z * e1 * zf_c / zs_c;
-    const float* rrow = a.R + srow * D;
 #pragma unroll
-    for (int d = 0; d < D; ++d) orow[d] = (o[d] * e1 + rrow[d] * e2) / den;
+    for (int d = 0; d < D; ++d) orow[d] = (o[d] * e1 + a.R[residual_index(bh, a.Nb, D, row, d)] * e2) / den;
   }
 }
 

@@ -10,6 +10,20 @@ constexpr int kMaxBlocks = 1024;   // Nb limit (N <= 65536)
 
 enum class AttnMode : int { kCalibrate = 0, kSparse = 1 };
 
+// Layout of the cached residual R (float32 or bf16 elements).  Each (b, h)
+// holds Nb blocks of 64 rows x D, rows past N being padding.  Inside a block
+// the element of row r and column c sits at
+//   ((r / 32 * D / 8 + c / 8) * 64 + 32 * (c / 4 % 2) + r % 32) * 4 + c % 4,
+// which is the order in which the 32x32 MFMA accumulators of a wave (rows
+// 32 * (r / 32) onwards) hold the block: the 4 elements one lane loads or
+// stores for an 8-column group are part of one contiguous run over the
+// wave's 64 lanes.
+__host__ __device__ inline size_t residual_index(size_t bh, int Nb, int D, int row, int col) {
+  const int r = row % kBlock;
+  const size_t block = (bh * (size_t)Nb + (size_t)(row / kBlock)) * (size_t)(kBlock * D);
+  return block + (size_t)((((r >> 5) * (D / 8) + (col >> 3)) * 64 + 32 * ((col >> 2) & 1) + (r & 31)) * 4 + (col & 3));
+}
+
 // Everything one attention launch needs.  Tensors are [BH, N, D] row-major.
 struct AttnArgs {
   const void* q;
@@ -21,7 +35,7 @@ struct AttnArgs {
   float* m;                // statistics cache rows [BH, N]
   float* z_full;
   float* z_sparse;
-  float* R;                // [BH, N, D]: float32, or bf16 when r_bf16
+  float* R;                // [BH, Nb * 64, D] in residual_index order: float32, or bf16 when r_bf16
   int32_t BH, N, Nb, keep;
   float alpha;             // 1/sqrt(d)
   int32_t r_bf16;          // residual stored as bf16 (bf16 kernels only)

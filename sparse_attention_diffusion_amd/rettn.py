@@ -55,6 +55,7 @@ def _load():
         "rt_stats_cache_bytes_ex": (SZ, [S, I32, I32]),
         "rt_stats_cache_init_ex": (I32, [ctypes.POINTER(P), S, I32, I32, P, SZ]),
         "rt_stats_cache_view": (I32, [P, I32, ctypes.POINTER(RtStatsView)]),
+        "rt_residual_index": (ctypes.c_int64, [S, ctypes.c_int64, I32, I32]),
         "rt_stats_cache_set_valid": (I32, [P, I32, I32]),
         "rt_stats_cache_invalidate": (I32, [P, I32]),
         "rt_stats_cache_destroy": (I32, [P]),
@@ -85,6 +86,7 @@ SYMBOLS = [
     "rt_stats_cache_set_valid", "rt_stats_cache_invalidate", "rt_stats_cache_destroy", "rt_calibrate",
     "rt_sparse_attn_reshape", "rt_sparse_attn_reshape_ex", "rt_schedule_is_calibration", "rt_step_workspace_bytes", "rt_attention_step",
     "rt_attention_step_ex", "rt_hilbert_order", "rt_permute_rows", "rt_select_blocks_noalloc",
+    "rt_residual_index",
 ]
 
 
@@ -167,6 +169,14 @@ def rt_select_blocks_noalloc(sh, q, k, forced, block_idx, pooled_scores, stream=
                                          _ptr(block_idx), _ptr(pooled_scores), _stream(stream)))
 
 
+def rt_residual_index(sh, bh, row, col):
+    """Element position of the residual of head bh, row, col from the view's R."""
+    at = _lib.rt_residual_index(ctypes.byref(sh), int(bh), int(row), int(col))
+    if at < 0:
+        raise RettnError(RT_E_ARG, _lib.rt_last_error().decode())
+    return at
+
+
 class StatsCache:
     """Host handle plus the device memory (a torch byte tensor) it wraps."""
 
@@ -189,7 +199,8 @@ class StatsCache:
         return v
 
     def tensors(self, layer=0):
-        """Zero-copy torch views of one layer: m, z_full, z_sparse [B,H,N]; R [B,H,N,d_pad]; idx [B,H,Nb,keep]."""
+        """Zero-copy torch views of one layer: m, z_full, z_sparse [B,H,N]; R flat, B*H*Nb*64*d_pad
+        elements in the order of rt_residual_index; idx [B,H,Nb,keep]."""
         v = self.view(layer)
         sh = self.shape
         nb = num_blocks(sh)
@@ -205,8 +216,8 @@ class StatsCache:
             m=sub(v.m, rows, torch.float32, (sh.B, sh.H, sh.N)),
             z_full=sub(v.z_full, rows, torch.float32, (sh.B, sh.H, sh.N)),
             z_sparse=sub(v.z_sparse, rows, torch.float32, (sh.B, sh.H, sh.N)),
-            R=sub(v.R, rows * sh.d_pad, torch.bfloat16 if v.r_dtype == 0 else torch.float32,
-                  (sh.B, sh.H, sh.N, sh.d_pad)),
+            R=sub(v.R, sh.B * sh.H * nb * 64 * sh.d_pad, torch.bfloat16 if v.r_dtype == 0 else torch.float32,
+                  (sh.B * sh.H * nb * 64 * sh.d_pad,)),
             idx=sub(v.idx, sh.B * sh.H * nb * sh.keep, torch.int32, (sh.B, sh.H, nb, sh.keep)),
             valid=v.valid,
         )

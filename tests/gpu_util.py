@@ -58,6 +58,46 @@ def host(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
+def residual_positions(sh, bh, rows):
+    """Positions in one layer's flat R of rows `rows` of head bh, all d_pad
+    columns ([len(rows), d_pad]).  The layout written out independently of
+    the library (and checked against its rt_residual_index on the host):
+    blocks of 64 rows padded past N; inside a block, for each 32-row half and
+    8-column group, a run of 256 elements ordered (4-column half, row, column)."""
+    D = sh.d_pad
+    nb = (sh.N + 63) // 64
+    row = np.asarray(rows, dtype=np.int64)[:, None]
+    col = np.arange(D, dtype=np.int64)[None, :]
+    r = row % 64
+    run = (r // 32) * (D // 8) + col // 8
+    return (bh * nb + row // 64) * 64 * D + run * 256 + (32 * ((col // 4) % 2) + r % 32) * 4 + col % 4
+
+
+def r_rows(R, sh, b, h, rows):
+    """Residual of head (b, h), rows `rows` (a slice or index array), as a host
+    float64 array [rows, d_pad]."""
+    pos = residual_positions(sh, b * sh.H + h, np.arange(sh.N)[rows])
+    return host(R[torch.as_tensor(pos, device=R.device)])
+
+
+def r_all(R, sh):
+    """The whole residual of one layer as a host float64 array [B, H, N, d_pad]."""
+    pos = np.stack([residual_positions(sh, bh, np.arange(sh.N)) for bh in range(sh.B * sh.H)])
+    return host(R[torch.as_tensor(pos, device=R.device)]).reshape(sh.B, sh.H, sh.N, sh.d_pad)
+
+
+def r_fill(R, sh, values):
+    """Stores values [B, H, N, c] (c <= d_pad; missing columns and the padding
+    rows become zero) into one layer's flat R."""
+    values = np.asarray(values)
+    full = np.zeros((sh.B, sh.H, sh.N, sh.d_pad), dtype=np.float64)
+    full[..., :values.shape[-1]] = values
+    pos = np.stack([residual_positions(sh, bh, np.arange(sh.N)) for bh in range(sh.B * sh.H)])
+    R.zero_()
+    R[torch.as_tensor(pos.reshape(-1), device=R.device)] = torch.as_tensor(full.reshape(-1), dtype=R.dtype,
+                                                                            device=R.device)
+
+
 def gpu_inputs(cfg, n_steps, seed=0):
     """Stored (q, k, v) per step, generated on the GPU."""
     return synth.steps(cfg, n_steps, seed=seed, device=DEV)

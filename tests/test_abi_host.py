@@ -52,7 +52,7 @@ def cache_bytes_expected(B, H, N, D, keep, layers):
     al = lambda x: (x + 255) // 256 * 256
     rows = B * H * N
     nb = (N + 63) // 64
-    per = 3 * al(rows * 4) + al(rows * D * 4) + al(B * H * nb * keep * 4)
+    per = 3 * al(rows * 4) + al(B * H * nb * 64 * D * 4) + al(B * H * nb * keep * 4)  # R padded to 64-row blocks
     return per * layers
 
 
@@ -120,7 +120,7 @@ def test_bf16_residual_cache_layout():
     """A bf16 residual halves the R section and nothing else; it needs bf16 q/k/v."""
     lib = rettn.lib()
     sh = rettn.shape(2, 3, 1000, 64, 64, 5, dtype="bf16")
-    rows = 2 * 3 * 1000
+    rows = 2 * 3 * 16 * 64  # R is padded to whole 64-row blocks: 16 blocks of 1000 rows
     f32 = rettn.stats_cache_bytes_ex(sh, 1, "f32")
     b16 = rettn.stats_cache_bytes_ex(sh, 1, "bf16")
     assert f32 == rettn.stats_cache_bytes(sh, 1)
@@ -357,3 +357,40 @@ def test_permute_rows_argument_errors():
     assert lib.rt_permute_rows(ctypes.byref(sh), p, q, None, 0, None) == rettn.RT_E_ARG
     if not torch.cuda.is_available():
         assert lib.rt_permute_rows(ctypes.byref(sh), p, q, p, 0, None) == rettn.RT_E_DEVICE
+
+
+def test_residual_index_matches_the_documented_layout():
+    """rt_residual_index against the layout written out in the tests' own code
+    (64-row blocks padded past N; in a block, one run of 256 elements per 32-row
+    half and 8-column group, ordered 4-column half, row, column): equal on every
+    element, one-to-one, inside the padded section, and out-of-range elements
+    refused."""
+    from tests import gpu_util as gu
+    for B, H, N, D in [(1, 2, 200, 64), (2, 1, 130, 80), (1, 1, 64, 64), (1, 1, 1, 80)]:
+        sh = rettn.shape(B, H, N, D, D, 1, "bf16")
+        nb = (N + 63) // 64
+        seen = []
+        for bh in range(B * H):
+            pos = gu.residual_positions(sh, bh, np.arange(N))
+            lib = np.array([[rettn.rt_residual_index(sh, bh, r, c) for c in range(D)] for r in range(N)])
+            assert np.array_equal(pos, lib), (B, H, N, D, bh)
+            seen.append(pos.reshape(-1))
+        seen = np.concatenate(seen)
+        assert len(np.unique(seen)) == seen.size and seen.min() >= 0 and seen.max() < B * H * nb * 64 * D
+        # a row's 8-column group is 4 runs of 4 contiguous elements, 128 apart (two 4-column halves)
+        assert list(gu.residual_positions(sh, 0, [0])[0, :8]) == [0, 1, 2, 3, 128, 129, 130, 131]
+        for bad in [(B * H, 0, 0), (-1, 0, 0), (0, N, 0), (0, -1, 0), (0, 0, D), (0, 0, -1)]:
+            with pytest.raises(rettn.RettnError):
+                rettn.rt_residual_index(sh, *bad)
+    # the section the view's R points at holds the padded block count
+    sh = rettn.shape(1, 3, 130, 80, 80, 2, "bf16")
+    buf, addr = _fake_dev_memory(rettn.stats_cache_bytes(sh, 1))
+    h = ctypes.c_void_p()
+    lib = rettn.lib()
+    assert lib.rt_stats_cache_init(ctypes.byref(h), ctypes.byref(sh), 1, ctypes.c_void_p(addr),
+                                   rettn.stats_cache_bytes(sh, 1)) == 0
+    v = rettn.RtStatsView()
+    assert lib.rt_stats_cache_view(h, 0, ctypes.byref(v)) == 0
+    assert v.idx - v.R >= 3 * 3 * 64 * 80 * 4
+    assert lib.rt_stats_cache_destroy(h) == 0
+    del buf

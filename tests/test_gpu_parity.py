@@ -142,7 +142,7 @@ def run_full_parity(cfg, steps_to_check, seed=0, residual="f32", variant=None):
     for zname in ("z_full", "z_sparse"):
         zr = np.abs(gu.host(t[zname]) / ref_cal[zname] - 1).max()
         assert zr <= 1e-4, (zname, zr)
-    r_l1 = np.abs(gu.host(t["R"]) - ref_cal["r"]).sum() / max(1e-30, np.abs(ref_cal["r"]).sum())
+    r_l1 = np.abs(gu.r_all(t["R"], sh) - ref_cal["r"]).sum() / max(1e-30, np.abs(ref_cal["r"]).sum())
     assert r_l1 <= 3e-3, r_l1
     for s in steps_to_check:
         q, k, v = stepsin[s]
@@ -209,7 +209,7 @@ def run_sampled_parity(cfg, heads, seed=0, n_steps=2, check_steps=(1,), residual
             assert np.abs(gu.host(t["m"][b, h, rows]) - st["m"]).max() <= 1e-4 * max(1, np.abs(st["m"]).max())
             assert np.abs(gu.host(t["z_full"][b, h, rows]) / st["z_full"] - 1).max() <= 1e-4
             assert np.abs(gu.host(t["z_sparse"][b, h, rows]) / st["z_sparse"] - 1).max() <= 1e-4
-            rl1 = np.abs(gu.host(t["R"][b, h, rows]) - st["r"]).sum() / np.abs(st["r"]).sum()
+            rl1 = np.abs(gu.r_rows(t["R"], sh, b, h, rows) - st["r"]).sum() / np.abs(st["r"]).sum()
             assert rl1 <= 3e-3, rl1
     for s in range(1, n_steps):
         q, k, v = (synth.store(x, cfg["dtype"]) for x in it.next())
@@ -235,12 +235,12 @@ def host32(t):
     return t.detach().float().cpu().numpy()
 
 
-def check_stats(t, b, h, rows, st, where):
+def check_stats(t, sh, b, h, rows, st, where):
     m = gu.host(t["m"][b, h, rows])
     assert np.abs(m - st["m"]).max() <= 1e-4 * max(1.0, np.abs(st["m"]).max()), ("m", where)
     for zname in ("z_full", "z_sparse"):
         assert np.abs(gu.host(t[zname][b, h, rows]) / st[zname] - 1).max() <= 1e-4, (zname, where)
-    r = gu.host(t["R"][b, h, rows])
+    r = gu.r_rows(t["R"], sh, b, h, rows)
     assert np.abs(r - st["r"]).sum() <= 3e-3 * max(1e-30, np.abs(st["r"]).sum()), ("R", where)
 
 
@@ -283,7 +283,7 @@ def test_parity_cogvideox2b_all_heads():
                 st = oracle.calibrate_rows(qh, kh, vh, rows, ref_idx[b, h, i], N, d)
                 refs[b, h, i] = st
                 w.add(ho[b, h, rows], st["o"], (b, h, i))
-                check_stats(t, b, h, rows, st, (b, h, i))
+                check_stats(t, sh, b, h, rows, st, (b, h, i))
     w.check()
     for s in range(1, 50):
         q, k, v = it.next_stored()
@@ -436,7 +436,7 @@ def test_sparse_kernel_with_oracle_cache(name):
     t = cache.tensors(0)
     for name_ in ("m", "z_full", "z_sparse"):
         t[name_].copy_(torch.as_tensor(ref_cal[name_], dtype=torch.float32))
-    t["R"].copy_(torch.as_tensor(ref_cal["r"], dtype=torch.float32))
+    gu.r_fill(t["R"], sh, ref_cal["r"])
     t["idx"].copy_(torch.as_tensor(ref_idx))
     cache.set_valid(0)
     o = gu.sparse(sh, q1, k1, v1, cache)  # lists from the cache
@@ -547,7 +547,7 @@ def test_sparse_many_blocks_per_workgroup(keep, variant):
     t["m"].copy_(torch.as_tensor(m_c, dtype=torch.float32))
     t["z_full"].copy_(torch.as_tensor(z_f, dtype=torch.float32))
     t["z_sparse"].copy_(torch.as_tensor(z_s, dtype=torch.float32))
-    t["R"].copy_(torch.as_tensor(r_c, dtype=torch.float32))
+    gu.r_fill(t["R"], sh, r_c)
     t["idx"].copy_(torch.as_tensor(idx))
     cache.set_valid(0)
     o = gu.sparse(sh, q, k, v, cache, variant=variant)
@@ -746,7 +746,7 @@ def test_cogvideox5b_full_schedule():
                             st = oracle.calibrate_rows(qh, kh, vh, rows, ref_list, N, d)
                             refs[b, h, i] = (st, ref_list)
                             w.add(ho[b, h, rows], st["o"], (b, h, i))
-                            check_stats(t, b, h, rows, st, (layer, s, b, h, i))
+                            check_stats(t, sh, b, h, rows, st, (layer, s, b, h, i))
                         elif (b, h, i) in refs:
                             st, ref_list = refs[b, h, i]
                             ro = oracle.sparse_reshape_rows(qh, kh, vh, rows, ref_list, st["m"], st["z_full"],
