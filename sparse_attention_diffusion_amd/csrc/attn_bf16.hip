@@ -512,8 +512,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 }
 
 
-// Tile DMA of one K or V tile, this wave's half (RSU/2 instructions of 1 KB);
-// same unit placement as TileDma.
+// Tile DMA of one 64-row tile (K, V or Q), this wave's half (RSU/2
+// instructions of 1 KB); same unit placement as TileDma.  Wave w fills tile
+// rows 32w..32w+31 (LDS bytes [32w ROW, 32(w+1) ROW)), so a wave that
+// overwrites only what it alone reads needs no barrier.
 template <int D>
 struct PipeDma {
   static constexpr int RSU = Shape<D>::RSU;
@@ -524,7 +526,7 @@ struct PipeDma {
     wave = w;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int L = 64 * (w + 2 * i) + lane;
+      const int L = 64 * (NI * w + i) + lane;
       const int r = L / RSU, p = L % RSU;
       int u = p < 8 ? (p ^ swz(r)) : p;
       if (u >= Shape<D>::UNITS) u -= 2;  // filler units of d_pad = 80 rows: any finite data
@@ -537,7 +539,7 @@ struct PipeDma {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, bytes);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + (wave + 2 * i) * 1024), 16, off[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + (NI * wave + i) * 1024), 16, off[i], 0, 0, 0);
   }
 };
 
@@ -566,16 +568,11 @@ struct PipeStats {
   float mc, zf, zs;
 };
 
-// Q^T operand and statistics of one query block: KS + 3 loads (KS + 2 for R2).
+// Statistics of one query block: 3 loads (2 for R2).
 template <int D, bool R2>
-__device__ __forceinline__ void load_qs(bf16x8 (&q)[Shape<D>::KS], PipeStats<D>& st, const AttnArgs& a, int bh,
-                                        int qi, int rowq, int g) {
+__device__ __forceinline__ void load_stats(PipeStats<D>& st, const AttnArgs& a, int bh, int qi, int rowq) {
   const size_t r0 = (size_t)bh * a.N + (size_t)qi * kBlock;  // first row of the block
   const int rows = min(a.N - qi * kBlock, kBlock);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)a.q + r0 * D * 2, rows * D * 2);
-#pragma unroll
-  for (int ks = 0; ks < Shape<D>::KS; ++ks)
-    q[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, (rowq * D + 16 * ks + 8 * g) * 2, 0, 0));
   if (!R2)
     st.mc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.m + r0, rows * 4), rowq * 4, 0, 0));
   st.zf = __builtin_bit_cast(float,
@@ -583,6 +580,9 @@ __device__ __forceinline__ void load_qs(bf16x8 (&q)[Shape<D>::KS], PipeStats<D>&
   st.zs = __builtin_bit_cast(float,
                              __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.z_sparse + r0, rows * 4), rowq * 4, 0, 0));
 }
+
+// Cache policy of the residual loads: non-temporal (read once per call).
+constexpr int kNT = 2;
 
 // Cached residual of one query block in accumulator order: D/8 loads.  The
 // cache holds it in that order (residual_index), padded to 64 rows, so every
@@ -606,11 +606,11 @@ __device__ __forceinline__ void load_residual(f32x4 (&r)[Shape<D>::NT][4], const
       if (32 * t + 8 * i4 >= D) {
         r[t][i4] = f32x4{};
       } else if (RB) {  // four bf16, widened exactly
-        const u32x2 h = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rr, lo + run, 0, 0));
+        const u32x2 h = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rr, lo + run, 0, kNT));
         r[t][i4] = f32x4{__uint_as_float(h[0] << 16), __uint_as_float(h[0] & 0xFFFF0000u),
                          __uint_as_float(h[1] << 16), __uint_as_float(h[1] & 0xFFFF0000u)};
       } else {
-        r[t][i4] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, lo + run, 0, 0));
+        r[t][i4] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, lo + run, 0, kNT));
       }
     }
 }
@@ -663,9 +663,8 @@ template <int D, bool RB, bool V2>
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 3, 4)))
 sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
   constexpr int NT = Shape<D>::NT, KS = Shape<D>::KS, TILE = Shape<D>::TILE, ROW = Shape<D>::ROW;
-  constexpr int NST = D / 16;         // O stores per lane (whole lines, staged through LDS)
-  constexpr int NRL = D / 8;          // residual loads per lane
-  constexpr int NLD = V2 ? KS + 2 : KS + NRL + 3;  // per-query-block loads (Q, statistics, R1: residual)
+  constexpr int NRL = D / 8;                  // residual loads per lane
+  constexpr int NLD = V2 ? 2 : NRL + 3;       // loads issued after a query block's Q (statistics, R1: residual)
   __shared__ __attribute__((aligned(1024))) char ring[2 * TILE];  // K slot, V slot
   char* const kslot = ring;
   char* const vslot = ring + TILE;
@@ -722,10 +721,15 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
   bf16x8 q[KS];
   f32x16 o[NT];
   PipeStats<D> st;
-  // Q, statistics and (R1) the residual, straight into the accumulator, of
-  // query block `it`: NLD loads.
+  // Q of query block `it` into the V slot, each wave its own 32 rows (read
+  // back at the block's first tile, before the wave's V DMA overwrites
+  // them), then the statistics and (R1) the residual, straight into the
+  // accumulator: NLD loads after the Q DMA.
+  const size_t qblk = (size_t)kBlock * D * 2;
   auto load_rows = [&]() {
-    load_qs<D, V2>(q, st, a, it.bh, it.qi, rowq, g);
+    dma.issue_at(vslot, (const char*)a.q + ((size_t)it.bh * N * D * 2 + (size_t)it.qi * qblk),
+                 min(N - it.qi * kBlock, kBlock) * D * 2);
+    load_stats<D, V2>(st, a, it.bh, it.qi, rowq);
     if (V2) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) o[t] = f32x16{};
@@ -745,10 +749,19 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
     int jprev = -1;  // a list entry equal to its predecessor is walked with every key masked
     for (int n = 0; n < keep; ++n) {
       // 1. K_n has landed (the loads issued after it may still be in flight).
-      if (n == 0 && k > 0) wait_vmcnt<NST + NLD>();
-      else if (n == 0) wait_vmcnt<NLD>();
-      else wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
+      //    At n = 0 the wave's Q rows have landed too: read them before the
+      //    wave's V DMA overwrites its half of the V slot.
+      if (n == 0) {
+        wait_vmcnt<NLD>();
+        __builtin_amdgcn_s_barrier();
+        u32x4 qq[KS];
+        k_half<KS>(qq, ka, TILE + wave * 32 * ROW);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) q[ks] = __builtin_bit_cast(bf16x8, qq[ks]);
+      } else {
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+      }
       dma.issue_at(vslot, vtile, tbytes);
       const int nvalid = j == jprev ? 0 : tbytes / (D * 2);
       jprev = j;
@@ -831,7 +844,7 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
       constexpr int RBYTES = D * 2;
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's V reads are done
       __builtin_amdgcn_s_barrier();
-      char* const stage = vslot + wave * 32 * RBYTES;
+      char* const stage = vslot + wave * 32 * ROW;  // this wave's half of the slot
       // Offsets are made opaque per query block so that the compiler keeps
       // one register for them rather than hoisting every derived address
       // out of the loop.
