@@ -94,6 +94,9 @@ UNIT_PASSES = [
     "GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_COEXEC_CYCLES",
     "GRBM_GUI_ACTIVE TA_TA_BUSY_sum TD_TD_BUSY_sum TCP_TCC_READ_REQ_sum TCP_TCC_READ_REQ_LATENCY_sum "
     "TCP_PENDING_STALL_CYCLES_sum",
+    "GRBM_GUI_ACTIVE SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_WAIT_INST_LDS "
+    "SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS",
+    "GRBM_GUI_ACTIVE SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_INSTS_VMEM SQ_INSTS_SMEM SQ_WAVES",
 ]
 
 
@@ -140,6 +143,21 @@ def unit_table(per):
         txt.append("–" if req is None else f"{req[0] / 1e6:.1f} M")
         txt.append("–" if not (req and lat) else f"{lat[0] / req[0]:.0f}")
         txt.append("–" if lat is None else f"{lat[0] / (lat[1] / XCDS * CUS):.0f}")
+        lines.append(f"| {label} | " + " | ".join(txt) + " |")
+    # wave states (fractions of the waves' lifetime) and instructions per MFMA
+    lines += ["", "| kernel | waiting on a counter (s_waitcnt) | ready, not issued | issuing | "
+              "VALU per MFMA | LDS per MFMA | SALU per MFMA | VMEM per MFMA |", "|---|---|---|---|---|---|---|---|"]
+    for label in sorted(per):
+        c = per[label]
+        wc = c.get("SQ_WAVE_CYCLES")
+        mf = c.get("SQ_INSTS_MFMA")
+        if wc is None and mf is None:
+            continue
+        st = [None if (wc is None or n not in c) else c[n][0] / wc[0]
+              for n in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY")]
+        mix = [None if (mf is None or not mf[0] or n not in c) else c[n][0] / mf[0]
+               for n in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM")]
+        txt = ["–" if x is None else f"{100 * x:.0f}%" for x in st] + ["–" if x is None else f"{x:.1f}" for x in mix]
         lines.append(f"| {label} | " + " | ".join(txt) + " |")
     return lines
 
