@@ -512,6 +512,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 }
 
 
+// Cache policy of the streams read once per call (Q, the residual): non-temporal.
+constexpr int kNT = 2;
+
 // Tile DMA of one 64-row tile (K, V or Q), this wave's half (RSU/2
 // instructions of 1 KB); same unit placement as TileDma.  Wave w fills tile
 // rows 32w..32w+31 (LDS bytes [32w ROW, 32(w+1) ROW)), so a wave that
@@ -533,13 +536,15 @@ struct PipeDma {
       off[i] = (uint32_t)((r * D + u * 8) * 2);
     }
   }
-  // A key-block tile (K or V) at `tile`, `bytes` of it valid, into `slot`;
-  // rows past the valid bytes are zero-filled by the buffer limit.
+  // A 64-row tile at `tile`, `bytes` of it valid, into `slot`; rows past the
+  // valid bytes are zero-filled by the buffer limit.  AUX is the cache policy
+  // (0, or kNT for a tile read once).
+  template <int AUX = 0>
   __device__ __forceinline__ void issue_at(char* slot, const char* tile, int bytes) const {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, bytes);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + (NI * wave + i) * 1024), 16, off[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + (NI * wave + i) * 1024), 16, off[i], 0, 0, AUX);
   }
 };
 
@@ -580,9 +585,6 @@ __device__ __forceinline__ void load_stats(PipeStats<D>& st, const AttnArgs& a, 
   st.zs = __builtin_bit_cast(float,
                              __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.z_sparse + r0, rows * 4), rowq * 4, 0, 0));
 }
-
-// Cache policy of the residual loads: non-temporal (read once per call).
-constexpr int kNT = 2;
 
 // Cached residual of one query block in accumulator order: D/8 loads.  The
 // cache holds it in that order (residual_index), padded to 64 rows, so every
@@ -727,8 +729,8 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
   // accumulator: NLD loads after the Q DMA.
   const size_t qblk = (size_t)kBlock * D * 2;
   auto load_rows = [&]() {
-    dma.issue_at(vslot, (const char*)a.q + ((size_t)it.bh * N * D * 2 + (size_t)it.qi * qblk),
-                 min(N - it.qi * kBlock, kBlock) * D * 2);
+    dma.template issue_at<kNT>(vslot, (const char*)a.q + ((size_t)it.bh * N * D * 2 + (size_t)it.qi * qblk),
+                               min(N - it.qi * kBlock, kBlock) * D * 2);
     load_stats<D, V2>(st, a, it.bh, it.qi, rowq);
     if (V2) {
 #pragma unroll

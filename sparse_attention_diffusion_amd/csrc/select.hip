@@ -166,6 +166,44 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x)
   return m;
 }
 
+// The same for N independent values, each step taken for all of them before
+// the next, so that their chains of lane exchanges overlap.
+template <int N>
+__device__ __forceinline__ void wave_max_u64_n(unsigned long long (&x)[N]) {
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const unsigned long long y = dpp_u64<0xB1>(x[n]);
+    x[n] = y > x[n] ? y : x[n];
+  }
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const unsigned long long y = dpp_u64<0x4E>(x[n]);
+    x[n] = y > x[n] ? y : x[n];
+  }
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const unsigned long long y = dpp_u64<0x141>(x[n]);
+    x[n] = y > x[n] ? y : x[n];
+  }
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const unsigned long long y = dpp_u64<0x140>(x[n]);
+    x[n] = y > x[n] ? y : x[n];
+  }
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    unsigned long long m = 0ull;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const unsigned lo = __builtin_amdgcn_readlane((unsigned)x[n], 16 * r);
+      const unsigned hi = __builtin_amdgcn_readlane((unsigned)(x[n] >> 32), 16 * r);
+      const unsigned long long v = ((unsigned long long)hi << 32) | lo;
+      m = v > m ? v : m;
+    }
+    x[n] = m;
+  }
+}
+
 // Orders this wave's LDS accesses: one wave's LDS instructions execute in
 // order, so every lane's earlier LDS writes are seen by later reads of any
 // lane once the compiler keeps them in program order; this is that compiler
@@ -183,8 +221,10 @@ constexpr int kMaxSelLds = 64 << 10;  // dynamic LDS of one selecting workgroup 
 template <int CH>
 constexpr int query_group() { return CH <= 8 ? 4 : 2; }
 
-// Dynamic LDS of select_kernel: a chunk of 64 blocks' K means [D][64]
-// floats shared by the workgroup, then per wave: pooled queries [QG][D],
+// Dynamic LDS of select_kernel: a chunk of 64 blocks' K means, one row of
+// D + 4 floats per block (16 bytes of padding keep a wave's 16-byte reads of
+// 64 rows free of bank conflicts), shared by the workgroup, then per wave:
+// pooled queries [QG][D],
 // pooling partials [RPI][D] (floats), one flag row (Nb rounded up to 16
 // bytes) and, for the bitonic fallback only, P 64-bit keys.
 struct SelectLds {
@@ -192,7 +232,7 @@ struct SelectLds {
 };
 inline SelectLds select_lds(int W, int QG, int D, int RPI, int Nb, bool bitonic) {
   SelectLds l;
-  l.kc_bytes = D * 64 * 4;
+  l.kc_bytes = (D + 4) * 64 * 4;
   l.q_off = 0;
   l.part_off = QG * D * 4;
   l.flag_off = l.part_off + RPI * D * 4;
@@ -241,7 +281,8 @@ __global__ void __launch_bounds__(64 * W) select_kernel(SelectArgs a, XcdGrid gr
   constexpr int QG = query_group<CH>();
   constexpr int E = Chunk<T>::E, CPR = D / E, RPI = 64 / CPR, PASSES = (kBlock + RPI - 1) / RPI;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  float(*kc)[64] = (float(*)[64])smem;
+  constexpr int KCS = D + 4;  // floats per key block row of the staged chunk
+  float* const kc = (float*)smem;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   char* wb = smem + lay.kc_bytes + wave * lay.wave_bytes;
@@ -334,7 +375,7 @@ __global__ void __launch_bounds__(64 * W) select_kernel(SelectArgs a, XcdGrid gr
 #pragma unroll
       for (int r = 0; r < PER; ++r) {
         const int e = (int)threadIdx.x + r * 64 * W;
-        kc[e >> 6][e & 63] = nxt[r];
+        kc[(e & 63) * KCS + (e >> 6)] = nxt[r];
       }
       __syncthreads();
       if (c + 1 < nc) load_chunk(c + 1);
@@ -343,9 +384,7 @@ __global__ void __launch_bounds__(64 * W) select_kernel(SelectArgs a, XcdGrid gr
       for (int g = 0; g < QG; ++g) acc[g] = 0.f;
 #pragma unroll
       for (int d0 = 0; d0 < D; d0 += 4) {
-        float kv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) kv[e] = kc[d0 + e][lane];
+        const f32x4 kv = *(const f32x4*)&kc[lane * KCS + d0];
 #pragma unroll
         for (int g = 0; g < QG; ++g) {
           const f32x4 qv = *(const f32x4*)&qrow[g][d0];
@@ -358,47 +397,87 @@ __global__ void __launch_bounds__(64 * W) select_kernel(SelectArgs a, XcdGrid gr
     }
   }
 
-  // 3. the kept list of each of the wave's query blocks
+  // 3. the kept lists.  64-bit keys: order-preserving score bits, then ~j
+  // (ties to the lower j); 0 marks no candidate (a forced block, a block past
+  // Nb, a query block the wave does not own).  Forced blocks take no round.
+  const int rounds = keep - n_forced;
+  if (a.scores) {
 #pragma unroll
-  for (int g = 0; g < QG; ++g) {
-    if (g >= nq) break;
-    const int i = i0 + g;
-    if (a.scores) {
+    for (int g = 0; g < QG; ++g) {
+      if (g >= nq) break;
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         const int j = c * 64 + lane;
-        if (c < nc && j < Nb) a.scores[((size_t)bh * Nb + i) * Nb + j] = sc[g][c];
+        if (c < nc && j < Nb) a.scores[((size_t)bh * Nb + i0 + g) * Nb + j] = sc[g][c];
       }
     }
-    // 64-bit keys: order-preserving score bits, then ~j (ties to the lower j);
-    // forced blocks are marked directly and take no round.
-    unsigned long long kk[CH];
+  }
+  auto is_forced = [&](int j) { return ((a.forced[j >> 5] >> (j & 31)) & 1u) != 0u; };
+  auto key_of = [&](int g, int c) {
+    const int j = c * 64 + lane;
+    return (g < nq && c < nc && j < Nb && !is_forced(j))
+               ? (((unsigned long long)order_key(sc[g][c]) << 32) | (0xFFFFFFFFu - (uint32_t)j))
+               : 0ull;
+  };
+  auto flag_forced = [&]() {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int j = c * 64 + lane;
-      kk[c] = 0ull;
-      if (c < nc && j < Nb) {
-        if ((a.forced[j >> 5] >> (j & 31)) & 1u) flags[j] = 1;
-        else kk[c] = ((unsigned long long)order_key(sc[g][c]) << 32) | (0xFFFFFFFFu - (uint32_t)j);
+      if (c < nc && j < Nb && is_forced(j)) flags[j] = 1;
+    }
+  };
+  auto emit_and_clear = [&](int g) {
+    wave_sync();
+    emit(flags, Nb, a.idx + ((size_t)bh * Nb + i0 + g) * keep);
+    wave_sync();
+    for (int e = lane; e < lay.flag_stride / 4; e += 64) ((uint32_t*)flags)[e] = 0u;  // for the next block
+    wave_sync();
+  };
+  if (rounds <= kMaxRounds) {
+    // The rounds of the wave's QG query blocks run side by side (independent
+    // chains of lane exchanges); lane t of win[g] keeps round t's winner of
+    // block g, -1 once no candidate is left (more rounds than blocks).
+    unsigned long long kk[QG][CH];
+    int win[QG];
+#pragma unroll
+    for (int g = 0; g < QG; ++g) {
+      win[g] = -1;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) kk[g][c] = key_of(g, c);
+    }
+    for (int t = 0; t < rounds; ++t) {
+      unsigned long long best[QG];
+#pragma unroll
+      for (int g = 0; g < QG; ++g) {
+        best[g] = 0ull;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) best[g] = kk[g][c] > best[g] ? kk[g][c] : best[g];
+      }
+      wave_max_u64_n<QG>(best);
+#pragma unroll
+      for (int g = 0; g < QG; ++g) {
+        const int jw = best[g] != 0ull ? (int)(0xFFFFFFFFu - (uint32_t)(best[g] & 0xFFFFFFFFull)) : -1;
+        if (lane == t) win[g] = jw;
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+          if (jw >= 0 && c == (jw >> 6) && lane == (jw & 63)) kk[g][c] = 0ull;
       }
     }
-    const int rounds = keep - n_forced;
-    if (rounds <= kMaxRounds) {
-      for (int t = 0; t < rounds; ++t) {
-        unsigned long long best = 0ull;
 #pragma unroll
-        for (int c = 0; c < CH; ++c) best = kk[c] > best ? kk[c] : best;
-        best = wave_max_u64(best);
-        if (best == 0ull) break;  // no candidate left (more rounds than blocks)
-        const int jw = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
-        if (lane == (jw & 63)) {
-          flags[jw] = 1;
+    for (int g = 0; g < QG; ++g) {
+      if (g >= nq) break;
+      flag_forced();
+      if (lane < rounds && win[g] >= 0) flags[win[g]] = 1;
+      emit_and_clear(g);
+    }
+  } else {
 #pragma unroll
-          for (int c = 0; c < CH; ++c)
-            if (c == (jw >> 6)) kk[c] = 0ull;
-        }
-      }
-    } else {
+    for (int g = 0; g < QG; ++g) {
+      if (g >= nq) break;
+      unsigned long long kk[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) kk[c] = key_of(g, c);
+      flag_forced();
       // Bitonic sort of the non-forced keys, descending, in this wave's LDS.
       int P = 64;
       while (P < Nb) P <<= 1;
@@ -428,12 +507,8 @@ __global__ void __launch_bounds__(64 * W) select_kernel(SelectArgs a, XcdGrid gr
       // a padding key (0) is still skipped rather than trusted.
       for (int t = lane; t < rounds; t += 64)
         if (keys[t] != 0ull) flags[0xFFFFFFFFu - (uint32_t)(keys[t] & 0xFFFFFFFFull)] = 1;
+      emit_and_clear(g);
     }
-    wave_sync();
-    emit(flags, Nb, a.idx + ((size_t)bh * Nb + i) * keep);
-    wave_sync();
-    for (int e = lane; e < lay.flag_stride / 4; e += 64) ((uint32_t*)flags)[e] = 0u;  // for the next block
-    wave_sync();
   }
 }
 

@@ -145,6 +145,8 @@ def unit_table(per):
         txt.append("–" if lat is None else f"{lat[0] / (lat[1] / XCDS * CUS):.0f}")
         lines.append(f"| {label} | " + " | ".join(txt) + " |")
     # wave states (fractions of the waves' lifetime) and instructions per MFMA
+    if not any("SQ_WAVE_CYCLES" in c or "SQ_INSTS_MFMA" in c for c in per.values()):
+        return lines
     lines += ["", "| kernel | waiting on a counter (s_waitcnt) | ready, not issued | issuing | "
               "VALU per MFMA | LDS per MFMA | SALU per MFMA | VMEM per MFMA |", "|---|---|---|---|---|---|---|---|"]
     for label in sorted(per):

@@ -99,3 +99,16 @@ def test_unit_utilisation_summary(tmp_path):
     rows = profsum.unit_table(profsum.unit_counters([str(d1), str(d2)]))
     cells = [x.strip() for x in rows[-1].split("|")[1:-1]]
     assert cells == ["sparse reshape R1 (d_pad 64)", "50%", "25%", "10%", "25%", "50%", "10%", "0.0 M", "512", "10"]
+    # wave states are fractions of SQ_WAVE_CYCLES; the instruction mix is per MFMA instruction
+    d3, d4 = tmp_path / "u3", tmp_path / "u4"
+    d3.mkdir()
+    d4.mkdir()
+    _write_csv(d3 / "run_counter_collection.csv", ["Kernel_Name", "Counter_Name", "Counter_Value"], [
+        [k, "GRBM_GUI_ACTIVE", 8000], [k, "SQ_WAVE_CYCLES", 1000], [k, "SQ_WAIT_ANY", 360],
+        [k, "SQ_WAIT_INST_ANY", 400], [k, "SQ_ACTIVE_INST_ANY", 230]])
+    _write_csv(d4 / "run_counter_collection.csv", ["Kernel_Name", "Counter_Name", "Counter_Value"], [
+        [k, "GRBM_GUI_ACTIVE", 8000], [k, "SQ_INSTS_MFMA", 100], [k, "SQ_INSTS_VALU", 1030],
+        [k, "SQ_INSTS_LDS", 160], [k, "SQ_INSTS_SALU", 450], [k, "SQ_INSTS_VMEM", 60]])
+    rows = profsum.unit_table(profsum.unit_counters([str(d1), str(d2), str(d3), str(d4)]))
+    cells = [x.strip() for x in rows[-1].split("|")[1:-1]]
+    assert cells == ["sparse reshape R1 (d_pad 64)", "36%", "40%", "23%", "10.3", "1.6", "4.5", "0.6"]
