@@ -668,6 +668,7 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
   constexpr int NRL = D / 8;                  // residual loads per lane
   constexpr int NLD = V2 ? 2 : NRL + 3;       // loads issued after a query block's Q (statistics, R1: residual)
   __shared__ __attribute__((aligned(1024))) char ring[2 * TILE];  // K slot, V slot
+  __shared__ int redo[2];  // per wave: a row of its 32 left the fixed reference's range
   char* const kslot = ring;
   char* const vslot = ring + TILE;
 
@@ -728,10 +729,8 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
   // them), then the statistics and (R1) the residual, straight into the
   // accumulator: NLD loads after the Q DMA.
   const size_t qblk = (size_t)kBlock * D * 2;
-  auto load_rows = [&]() {
-    dma.template issue_at<kNT>(vslot, (const char*)a.q + ((size_t)it.bh * N * D * 2 + (size_t)it.qi * qblk),
-                               min(N - it.qi * kBlock, kBlock) * D * 2);
-    load_stats<D, V2>(st, a, it.bh, it.qi, rowq);
+  // The accumulator's starting value: the cached residual (R1), or zero.
+  auto init_acc = [&]() {
     if (V2) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) o[t] = f32x16{};
@@ -744,10 +743,50 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
         for (int i = 0; i < 16; ++i) o[t][i] = r[t][i >> 2][i & 3];
     }
   };
+  // S^T = K Q^T of the tile in the K slot, one 32-key half at a time.
+  auto tile_scores = [&](f32x16 (&s)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      u32x4 kk[KS];
+      k_half<KS>(kk, ka, t * 32 * ROW);
+      s[t] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kk[ks]), q[ks], s[t], 0, 0, 0);
+    }
+  };
+  // O^T += V^T P^T with the tile in the V slot, one d tile at a time.
+  auto tile_pv = [&](const bf16x8 (&p)[2][2]) {
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) {
+      u32x2 h[2][2][2];
+      tr_reads<0, 32 * ROW, 16 * ROW>(h, va[dt][0], va[dt][1]);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          const u32x4 both = __builtin_shufflevector(h[t][hs][0], h[t][hs][1], 0, 1, 2, 3);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), p[t][hs], o[dt], 0, 0, 0);
+        }
+    }
+  };
+  auto load_rows = [&]() {
+    dma.template issue_at<kNT>(vslot, (const char*)a.q + ((size_t)it.bh * N * D * 2 + (size_t)it.qi * qblk),
+                               min(N - it.qi * kBlock, kBlock) * D * 2);
+    load_stats<D, V2>(st, a, it.bh, it.qi, rowq);
+    init_acc();
+  };
   load_rows();
 
   for (int k = 0; k < n_items; ++k) {
-    float mr = V2 ? -INFINITY : st.mc * kLog2e, z = 0.f;
+    float mr, z;
+    // The per-tile maximum: on the block's second walk, and always at d_pad 80
+    // (whose calls are latency-bound and have no registers to spare for the
+    // redo path).
+    bool careful = D != 64;
+    for (;;) {
+    mr = V2 ? -INFINITY : st.mc * kLog2e;
+    z = 0.f;
     int jprev = -1;  // a list entry equal to its predecessor is walked with every key masked
     for (int n = 0; n < keep; ++n) {
       // 1. K_n has landed (the loads issued after it may still be in flight).
@@ -767,26 +806,25 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
       dma.issue_at(vslot, vtile, tbytes);
       const int nvalid = j == jprev ? 0 : tbytes / (D * 2);
       jprev = j;
-      // 2. scores and P, one 32-key half at a time.
+      // 2. scores and P against the reference mr: the cached row max (R1) or,
+      //    for R2, the row max of the block's first tile (it always holds a
+      //    valid key).  The first walk takes no per-tile maximum; a row that
+      //    leaves the float32 range there is caught after the block, and the
+      //    block is walked again with the lazy maximum (raise the reference
+      //    when a tile's row max passes it by a factor 2^8).
       f32x16 s[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        u32x4 kk[KS];
-        k_half<KS>(kk, ka, t * 32 * ROW);
-        s[t] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kk[ks]), q[ks], s[t], 0, 0, 0);
-      }
+      tile_scores(s);
       if (nvalid < kBlock) mask_keys<D>(s, nvalid);
-      const float mx = row_max(s) * c;
-      if (__ballot(mx > mr + kLazyLog2) != 0ull) {
-        const float mnew = fmaxf(mr, mx);
-        const float corr = __builtin_amdgcn_exp2f(mr - mnew);
-        mr = mnew;
-        z *= corr;
+      if (careful || (V2 && n == 0)) {
+        const float mx = row_max(s) * c;
+        if (__ballot(mx > mr + kLazyLog2) != 0ull) {
+          const float mnew = fmaxf(mr, mx);
+          const float corr = __builtin_amdgcn_exp2f(mr - mnew);
+          mr = mnew;
+          z *= corr;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) o[t] *= corr;
+          for (int t = 0; t < NT; ++t) o[t] *= corr;
+        }
       }
       bf16x8 p[2][2];
       probs_ref(p, s, mr, c);
@@ -810,19 +848,31 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
           jnext = t2.block(0, Nb);
         }
       }
-      // 4. P.V, one d tile at a time.
-#pragma unroll
-      for (int dt = 0; dt < NT; ++dt) {
-        u32x2 h[2][2][2];
-        tr_reads<0, 32 * ROW, 16 * ROW>(h, va[dt][0], va[dt][1]);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int hs = 0; hs < 2; ++hs) {
-            const u32x4 both = __builtin_shufflevector(h[t][hs][0], h[t][hs][1], 0, 1, 2, 3);
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), p[t][hs], o[dt], 0, 0, 0);
-          }
-      }
+      // 4. P.V
+      tile_pv(p);
+    }
+    // A row sum at 2^64 or more, or not finite, means a score rose far enough
+    // above the reference for P or the accumulator to overflow: both waves
+    // walk the block again with the per-tile maximum.
+    if (careful) break;
+    if (lane == 0) redo[wave] = __ballot(!(pair_sum(z) < 0x1p64f)) != 0ull;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    if ((redo[0] | redo[1]) != 0) {
+      // Back to this block's first tile: drain, its first K again, then its Q,
+      // statistics and accumulator in the same order as for a new block.
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      j = it.block(0, Nb);
+      jnext = keep > 1 ? it.block(1, Nb) : nit.block(0, Nb);
+      tbytes = min(N - j * kBlock, kBlock) * D * 2;
+      vtile = it.vh + (size_t)j * blk;
+      dma.issue_at(kslot, it.kh + (size_t)j * blk, tbytes);
+      load_rows();
+      careful = true;
+      continue;
+    }
+    break;
     }
     // O = acc * Z_sparse / (Z * Z_full) (+ R / Z_full for R2); rows past N
     // are dropped by the limit.

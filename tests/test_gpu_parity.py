@@ -567,6 +567,66 @@ def test_sparse_many_blocks_per_workgroup(keep, variant):
     gu.assert_close(np.concatenate(got), np.concatenate(ref))
 
 
+@pytest.mark.parametrize("variant", ["r1", "r2"])
+def test_sparse_rows_beyond_the_reference_range(variant):
+    """Rows whose scores rise far above the reference the first walk takes P
+    against: the cached row max (R1; set 200 below the scores for one head) or
+    the first listed tile's row max (R2; every list of six heads ends with a
+    key block scaled by 40, whose scores exceed the first tile's by far more
+    than float32 exponentials hold).  Those blocks overflow on the first walk
+    and are walked again with the per-tile maximum; with several query blocks
+    per workgroup the blocks after a redone one must come out right too.  All
+    sampled blocks are compared with the oracle."""
+    say("sparse rows beyond the reference range", variant)
+    B, H, d, keep = 2, 16, 64, 5
+    N = 64 * 170 + 23
+    nb = (N + 63) // 64
+    hot = nb - 3
+    q, k, v = synth.random_qkv(B, H, N, d, d, seed=123, scale=1.0, dtype="bf16", device=gu.DEV)
+    k[:, :6, hot * 64:(hot + 1) * 64] *= 40.0
+    g = np.random.default_rng(11)
+    idx = np.empty((B, H, nb, keep), dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nb):
+                pool = np.delete(np.arange(nb), hot)
+                row = g.choice(pool, keep - 1 if h < 6 else keep, replace=False)
+                idx[b, h, i] = np.sort(np.append(row, hot) if h < 6 else row)
+    m_c = g.uniform(-2.0, 6.0, (B, H, N))
+    m_c[:, 7] = -200.0
+    z_s = g.uniform(0.5, 2.0, (B, H, N))
+    z_f = z_s * g.uniform(1.0, 4.0, (B, H, N))
+    r_c = g.normal(0.0, 0.5, (B, H, N, d))
+    sh = rettn.shape(B, H, N, d, d, keep, "bf16")
+    cache = rettn.StatsCache(sh, 1)
+    t = cache.tensors(0)
+    t["m"].copy_(torch.as_tensor(m_c, dtype=torch.float32))
+    t["z_full"].copy_(torch.as_tensor(z_f, dtype=torch.float32))
+    t["z_sparse"].copy_(torch.as_tensor(z_s, dtype=torch.float32))
+    gu.r_fill(t["R"], sh, r_c)
+    t["idx"].copy_(torch.as_tensor(idx))
+    cache.set_valid(0)
+    o = gu.sparse(sh, q, k, v, cache, variant=variant)
+    torch.cuda.synchronize()
+    m32, zf32, zs32, r32 = (x.astype(np.float32) for x in (m_c, z_f, z_s, r_c))
+    qh, kh, vh, oh = gu.host(q), gu.host(k), gu.host(v), gu.host(o)
+    # the data does leave the range: scores of the hot block exceed those of a
+    # list's first block by more than 88 (e^88 is near the float32 limit)
+    s_first = qh[0, 0, :64] @ kh[0, 0, idx[0, 0, 0, 0] * 64:idx[0, 0, 0, 0] * 64 + 64].T / np.sqrt(d)
+    s_hot = qh[0, 0, :64] @ kh[0, 0, hot * 64:(hot + 1) * 64].T / np.sqrt(d)
+    assert (s_hot.max(axis=1) - s_first.max(axis=1)).max() > 88.0
+    got, ref = [], []
+    for b in range(B):
+        for h in range(H):
+            for a in list(g.choice(nb - 1, 3, replace=False)) + [0, nb - 1]:
+                rows = slice(64 * a, min(64 * a + 64, N))
+                st = {"m": m32[b, h, rows], "z_full": zf32[b, h, rows], "z_sparse": zs32[b, h, rows]}
+                ref.append(oracle_rows(variant, qh[b, h], kh[b, h], vh[b, h], rows, idx[b, h, a], st,
+                                       r32[b, h, rows], N, d))
+                got.append(oh[b, h, rows])
+    gu.assert_close(np.concatenate(got), np.concatenate(ref))
+
+
 @pytest.mark.parametrize("dtype,D,d", [("bf16", 64, 64), ("bf16", 80, 72), ("f32", 64, 64)])
 def test_repeated_list_entries_count_once(dtype, D, d):
     """A non-decreasing list with repeated entries is read as the set of its
