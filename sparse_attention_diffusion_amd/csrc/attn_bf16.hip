@@ -542,9 +542,16 @@ struct PipeDma {
   template <int AUX = 0>
   __device__ __forceinline__ void issue_at(char* slot, const char* tile, int bytes) const {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, bytes);
+    // The wave's first destination, kept opaque so that the compiler adds
+    // the 1 KB steps at each call instead of holding (and spilling) one
+    // scalar register per destination for the whole kernel.
+    uint32_t dst = lds_addr(slot) + (uint32_t)(NI * wave * 1024);
+    asm volatile("" : "+s"(dst));
+    lds_void* const d0 = (lds_void*)(uintptr_t)dst;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + (NI * wave + i) * 1024), 16, off[i], 0, 0, AUX);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)((__attribute__((address_space(3))) char*)d0 + i * 1024),
+                                               16, off[i], 0, 0, AUX);
   }
 };
 
