@@ -653,21 +653,25 @@ __device__ __forceinline__ void probs_ref(bf16x8 (&p)[2][2], const f32x16 (&s)[2
 // deep ring, which the LDS could not hold (each wave's vmcnt is one in-order
 // counter, so any long-latency load a wave issues delays its next tile wait).
 // Per key block n of a query block:
-//   1. wait for K_n, barrier (V_{n-1} consumed by both waves), DMA V_n;
-//   2. S^T = K_n Q^T in two 32-key halves, softmax with the lazy max;
+//   1. wait for K_n, barrier (V_{n-1} consumed by both waves), DMA V_n (at
+//      n = 0 each wave first reads its Q rows, DMA'd into its half of the V
+//      slot);
+//   2. S^T = K_n Q^T in two 32-key halves and P against a reference max;
 //   3. wait for V_n, barrier (K_n consumed), DMA K_{n+1} (which may belong to
 //      the next query block);
 //   4. O^T += V_n^T P^T.
 // A query block's accumulator starts as its cached residual R with the
-// reference max at the cached m (R is stored relative to m); the lazy max
-// update rescales both parts together, so the reshape epilogue is
-// O = acc * Z_sparse / (Z * Z_full) with Z the kept mass.
-// Variant R2 (V2) instead blends the normalised sparse output with the cached
-// masked output: the accumulator starts at zero with no reference max, the
-// residual is fetched in the epilogue, which computes
-// O = acc * Z_sparse / (Z * Z_full) + R / Z_full.  All global traffic goes
-// through buffer resources whose byte limit zero-fills rows past N on loads
-// and drops them on stores.
+// reference max at the cached m (R is stored relative to m), so the reshape
+// epilogue is O = acc * Z_sparse / (Z * Z_full) with Z the kept mass.  At
+// d_pad 64 the first walk keeps that reference fixed (no per-tile maximum);
+// a row sum that leaves the float32 range sends the block through a second
+// walk with the lazy maximum, which rescales both parts together.  Variant R2
+// (V2) instead blends the normalised sparse output with the cached masked
+// output: the accumulator starts at zero, the reference is the first tile's
+// row max, and the residual is fetched in the epilogue, which computes
+// O = acc * Z_sparse / (Z * Z_full) + R / Z_full.  O leaves through the V
+// slot as whole lines.  All global traffic goes through buffer resources
+// whose byte limit zero-fills rows past N on loads and drops them on stores.
 template <int D, bool RB, bool V2>
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 3, 4)))
 sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
