@@ -47,6 +47,14 @@ int main(void) {
   CHECK(strlen(rt_last_error()) > 0);
   CHECK(rt_stats_cache_destroy(c) == RT_OK);
 
+  /* residual layout: row 33 is in the second 32-row half of block 0, column 9
+     in the second 8-column group, first 4-column half: ((1*8 + 1)*64 + 1)*4 + 1;
+     row 17775 is row 47 of block 277 of head 59 */
+  CHECK(rt_residual_index(&sh, 0, 33, 9) == 2309);
+  CHECK(rt_residual_index(&sh, 59, 17775, 63) ==
+        ((int64_t)59 * 278 + 277) * 64 * 64 + ((1 * 8 + 7) * 64 + 32 + 15) * 4 + 3);
+  CHECK(rt_residual_index(&sh, 60, 0, 0) == -1 && rt_residual_index(&sh, 0, 17776, 0) == -1);
+
   /* shape validation */
   rt_shape bad = sh;
   bad.block = 32;
