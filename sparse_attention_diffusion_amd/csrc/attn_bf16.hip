@@ -91,6 +91,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
+// ---------------------------------------------------------------- buffer-resource helpers
+// Global traffic of the sparse kernel goes through buffer resources: per-lane
+// offsets are fixed, the base and the byte limit are scalar, and the limit
+// zero-fills rows past N on loads and drops them on stores.
+constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format (descriptor word 3)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufFlags);
+}
+
 // ------------------------------------------------------------------ DMA of tiles
 // A tile pair (K and V of one key block) is 2*RSU DMA instructions of 1 KB
 // (64 lanes x 16 B).  Wave w of W takes the K instructions c = w, w+W, ... and
@@ -104,7 +114,6 @@ struct TileDma {
   static constexpr int NI = RSU / W;  // K (and V) instructions per wave
   static constexpr int IPT = 2 * NI;  // DMA instructions per tile per wave
   uint32_t off[NI];
-  int row[NI];
   int wave;
 
   __device__ __forceinline__ void init(int w, int lane) {
@@ -115,32 +124,22 @@ struct TileDma {
       const int r = L / RSU, p = L % RSU;
       int u = p < 8 ? (p ^ swz(r)) : p;
       if (u >= Shape<D>::UNITS) u -= 2;  // filler units of d_pad = 80 rows: any finite data
-      row[i] = r;
       off[i] = (uint32_t)((r * D + u * 8) * 2);
     }
   }
-  // Key block j of the head at (kbase, vbase) into the slot at `slot`; keys
-  // past N read row N-1 (finite data; their scores are masked).
+  // Key block j of the head at (kbase, vbase) into the slot at `slot`,
+  // through buffer resources (scalar base and byte limit, fixed per-lane
+  // offsets): keys past N read as zeros (their scores are masked).
   __device__ __forceinline__ void issue(char* slot, const char* kbase, const char* vbase, int j, int N) const {
     const size_t blk = (size_t)j * kBlock * D * 2;
-    const char* kb = kbase + blk;
-    const char* vb = vbase + blk;
-    const int nvalid = N - j * kBlock;
-    if (nvalid >= kBlock) {  // uniform: every block but a short last one
+    const int bytes = min(N - j * kBlock, kBlock) * D * 2;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + blk, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + blk, bytes);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        char* dst = slot + (wave + W * i) * 1024;
-        __builtin_amdgcn_global_load_lds((const void*)(kb + off[i]), (lds_void*)dst, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vb + off[i]), (lds_void*)(dst + Shape<D>::TILE), 16, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const uint32_t o = off[i] - (uint32_t)(max(0, row[i] - (nvalid - 1)) * D * 2);
-        char* dst = slot + (wave + W * i) * 1024;
-        __builtin_amdgcn_global_load_lds((const void*)(kb + o), (lds_void*)dst, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vb + o), (lds_void*)(dst + Shape<D>::TILE), 16, 0, 0);
-      }
+    for (int i = 0; i < NI; ++i) {
+      char* dst = slot + (wave + W * i) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)dst, 16, (int)off[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst + Shape<D>::TILE), 16, (int)off[i], 0, 0, 0);
     }
   }
 };
@@ -501,15 +500,6 @@ struct PersistGrid {
   uint32_t total, per, g;  // query blocks, per XCD, workgroups per XCD
 };
 
-// ---------------------------------------------------------------- buffer-resource helpers
-// Global traffic of the sparse kernel goes through buffer resources: per-lane
-// offsets are fixed, the base and the byte limit are scalar, and the limit
-// zero-fills rows past N on loads and drops them on stores.
-constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format (descriptor word 3)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufFlags);
-}
 
 
 // Cache policy of the streams read once per call (Q, the residual): non-temporal.
