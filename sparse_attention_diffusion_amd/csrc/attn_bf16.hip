@@ -561,6 +561,9 @@ struct PipeItem {
     list = (const __attribute__((address_space(4))) int32_t*)(a.idx + (size_t)l * a.keep);
   }
   __device__ __forceinline__ int block(int n, int Nb) const { return min(max(list[n], 0), Nb - 1); }
+  // The list entry as stored; clamped where it is used, so that the wait for
+  // the scalar load falls there and not right after the load.
+  __device__ __forceinline__ int raw(int n) const { return list[n]; }
 };
 
 // One query block's per-lane statistics (the cached row max only for the
@@ -713,11 +716,12 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
   PipeItem<D> it, nit;  // query block being computed, and the next one
   it.set(a, item_at(0));
   nit.set(a, item_at(min(1, n_items - 1)));
-  // Tile whose K went out last: its V tile and valid bytes.  The block index
-  // of the tile after it is read one tile ahead (scalar loads: no wait at use).
+  // Tile whose K went out last: its V tile and valid bytes.  The list entry
+  // of the tile after it is read one tile ahead and clamped only when used.
   const size_t blk = (size_t)kBlock * D * 2;
+  auto clampb = [&](int x) { return min(max(x, 0), Nb - 1); };
   int j = it.block(0, Nb);
-  int jnext = keep > 1 ? it.block(1, Nb) : nit.block(0, Nb);
+  int jnext = keep > 1 ? it.raw(1) : nit.raw(0);
   int tbytes = min(N - j * kBlock, kBlock) * D * 2;
   const char* vtile = it.vh + (size_t)j * blk;
   dma.issue_at(kslot, it.kh + (size_t)j * blk, tbytes);  // K of the first tile
@@ -835,18 +839,18 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
       __builtin_amdgcn_s_barrier();
       if (n + 1 < keep || k + 1 < n_items) {
         const bool same = n + 1 < keep;  // the next tile is in this query block
-        j = jnext;
+        j = clampb(jnext);
         tbytes = min(N - j * kBlock, kBlock) * D * 2;
         vtile = (same ? it.vh : nit.vh) + (size_t)j * blk;
         dma.issue_at(kslot, (same ? it.kh : nit.kh) + (size_t)j * blk, tbytes);
-        // block index of the tile after it
-        if (n + 2 < keep) jnext = it.block(n + 2, Nb);
-        else if (n + 2 == keep) jnext = nit.block(0, Nb);
-        else if (keep > 1) jnext = nit.block(1, Nb);
+        // list entry of the tile after it
+        if (n + 2 < keep) jnext = it.raw(n + 2);
+        else if (n + 2 == keep) jnext = nit.raw(0);
+        else if (keep > 1) jnext = nit.raw(1);
         else {  // one block per query block: the block after next
           PipeItem<D> t2;
           t2.set(a, item_at(min(k + 2, n_items - 1)));
-          jnext = t2.block(0, Nb);
+          jnext = t2.raw(0);
         }
       }
       // 4. P.V
@@ -865,7 +869,7 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
       wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
       j = it.block(0, Nb);
-      jnext = keep > 1 ? it.block(1, Nb) : nit.block(0, Nb);
+      jnext = keep > 1 ? it.raw(1) : nit.raw(0);
       tbytes = min(N - j * kBlock, kBlock) * D * 2;
       vtile = it.vh + (size_t)j * blk;
       dma.issue_at(kslot, it.kh + (size_t)j * blk, tbytes);
