@@ -135,12 +135,14 @@ struct TileDma {
     const int bytes = min(N - j * kBlock, kBlock) * D * 2;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + blk, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + blk, bytes);
+    asm volatile("" ::: "memory");  // in program order with other memory operations (vmcnt counts)
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       char* dst = slot + (wave + W * i) * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)dst, 16, (int)off[i], 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst + Shape<D>::TILE), 16, (int)off[i], 0, 0, 0);
     }
+    asm volatile("" ::: "memory");
   }
 };
 
@@ -538,10 +540,14 @@ struct PipeDma {
     uint32_t dst = lds_addr(slot) + (uint32_t)(NI * wave * 1024);
     asm volatile("" : "+s"(dst));
     lds_void* const d0 = (lds_void*)(uintptr_t)dst;
+    // The batch stays in program order with every other memory operation:
+    // the vmcnt waits count instructions issued after it.
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)((__attribute__((address_space(3))) char*)d0 + i * 1024),
                                                16, off[i], 0, 0, AUX);
+    asm volatile("" ::: "memory");
   }
 };
 
@@ -687,6 +693,23 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
   const int rowq = wave * 32 + l32;  // row within the query block
   const float c = a.alpha * kLog2e;
   auto item_at = [&](int k) { return start + rr + (uint32_t)k * pg.g; };
+  // The arguments used once per query block (tensor and cache pointers) are
+  // read again from the kernel-argument segment where they are used, with
+  // scalar loads, instead of being held in scalar registers (and spilled) for
+  // the whole kernel.
+  auto args = [&]() {
+    typedef const __attribute__((address_space(4))) AttnArgs* kptr;
+    kptr p = (kptr)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(p));
+    static_assert(sizeof(AttnArgs) == 112, "the copy below names every field of AttnArgs");
+    AttnArgs r;
+    r.q = p->q; r.k = p->k; r.v = p->v; r.o = p->o;
+    r.idx = p->idx; r.idx_cache = p->idx_cache;
+    r.m = p->m; r.z_full = p->z_full; r.z_sparse = p->z_sparse; r.R = p->R;
+    r.BH = p->BH; r.N = p->N; r.Nb = p->Nb; r.keep = p->keep;
+    r.alpha = p->alpha; r.r_bf16 = p->r_bf16; r.variant = p->variant;
+    return r;
+  };
 
   // LDS that no DMA has written yet must still read as finite numbers.
   {
@@ -741,7 +764,7 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
       for (int t = 0; t < NT; ++t) o[t] = f32x16{};
     } else {
       f32x4 r[NT][4];
-      load_residual<D, RB>(r, a, it.bh, it.qi, rowq, g);
+      load_residual<D, RB>(r, args(), it.bh, it.qi, rowq, g);
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -776,9 +799,10 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
     }
   };
   auto load_rows = [&]() {
-    dma.template issue_at<kNT>(vslot, (const char*)a.q + ((size_t)it.bh * N * D * 2 + (size_t)it.qi * qblk),
+    const AttnArgs aa = args();
+    dma.template issue_at<kNT>(vslot, (const char*)aa.q + ((size_t)it.bh * N * D * 2 + (size_t)it.qi * qblk),
                                min(N - it.qi * kBlock, kBlock) * D * 2);
-    load_stats<D, V2>(st, a, it.bh, it.qi, rowq);
+    load_stats<D, V2>(st, aa, it.bh, it.qi, rowq);
     init_acc();
   };
   load_rows();
@@ -849,7 +873,7 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
         else if (keep > 1) jnext = nit.raw(1);
         else {  // one block per query block: the block after next
           PipeItem<D> t2;
-          t2.set(a, item_at(min(k + 2, n_items - 1)));
+          t2.set(args(), item_at(min(k + 2, n_items - 1)));
           jnext = t2.raw(0);
         }
       }
@@ -860,7 +884,8 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
     // above the reference for P or the accumulator to overflow: both waves
     // walk the block again with the per-tile maximum.
     if (careful) break;
-    if (lane == 0) redo[wave] = __ballot(!(pair_sum(z) < 0x1p64f)) != 0ull;
+    const bool bad = __ballot(!(pair_sum(z) < 0x1p64f)) != 0ull;  // every lane's row, all lanes active
+    if (lane == 0) redo[wave] = bad;
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     if ((redo[0] | redo[1]) != 0) {
@@ -886,11 +911,12 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
       const float u = 1.f / st.zf;
       f32x4 rv[NT][4];  // R2: the residual, fetched now (no registers are free during the tiles)
       if (V2) {
-        load_residual<D, RB>(rv, a, it.bh, it.qi, rowq, g);
+        load_residual<D, RB>(rv, args(), it.bh, it.qi, rowq, g);
         wait_vmcnt<0>();
       }
       const size_t r0 = (size_t)it.bh * N + (size_t)it.qi * kBlock;
-      const __amdgpu_buffer_rsrc_t ro = make_rsrc((const char*)a.o + r0 * D * 2, min(N - it.qi * kBlock, kBlock) * D * 2);
+      const __amdgpu_buffer_rsrc_t ro =
+          make_rsrc((const char*)args().o + r0 * D * 2, min(N - it.qi * kBlock, kBlock) * D * 2);
       // The output goes through the V slot (free once both waves are past
       // their last P.V): each wave writes its 32 rows there in the MFMA
       // layout, reads them back row-contiguous and stores whole 128-byte
@@ -933,7 +959,7 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
     }
     if (k + 1 < n_items) {
       it = nit;
-      nit.set(a, item_at(min(k + 2, n_items - 1)));
+      nit.set(args(), item_at(min(k + 2, n_items - 1)));
       load_rows();
     }
   }
