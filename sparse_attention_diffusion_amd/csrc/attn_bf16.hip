@@ -65,6 +65,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// Workgroup barrier that the compiler also treats as a memory barrier: no
+// load or store (LDS or global) moves across it, so the LDS a barrier guards
+// (tiles, staged rows, flags) is read and written on the intended side.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Waits until the tile of this step has landed, allowing `younger` later tiles
 // (IPT DMA instructions each) to stay in flight.  Any other memory operation
 // issued after the tile only makes the wait longer, never too short.
@@ -823,14 +832,14 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
       //    wave's V DMA overwrites its half of the V slot.
       if (n == 0) {
         wait_vmcnt<NLD>();
-        __builtin_amdgcn_s_barrier();
+        wg_barrier();
         u32x4 qq[KS];
         k_half<KS>(qq, ka, TILE + wave * 32 * ROW);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) q[ks] = __builtin_bit_cast(bf16x8, qq[ks]);
       } else {
         wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
+        wg_barrier();
       }
       dma.issue_at(vslot, vtile, tbytes);
       const int nvalid = j == jprev ? 0 : tbytes / (D * 2);
@@ -860,7 +869,7 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
       z += sum_rounded(p);
       // 3. V_n has landed; K_n is consumed: K of the next tile goes out.
       wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
+      wg_barrier();
       if (n + 1 < keep || k + 1 < n_items) {
         const bool same = n + 1 < keep;  // the next tile is in this query block
         j = clampb(jnext);
@@ -887,12 +896,12 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
     const bool bad = __ballot(!(pair_sum(z) < 0x1p64f)) != 0ull;  // every lane's row, all lanes active
     if (lane == 0) redo[wave] = bad;
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
+    wg_barrier();
     if ((redo[0] | redo[1]) != 0) {
       // Back to this block's first tile: drain, its first K again, then its Q,
       // statistics and accumulator in the same order as for a new block.
       wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
+      wg_barrier();
       j = it.block(0, Nb);
       jnext = keep > 1 ? it.raw(1) : nit.raw(0);
       tbytes = min(N - j * kBlock, kBlock) * D * 2;
@@ -926,7 +935,7 @@ sparse_occ_kernel(AttnArgs a, PersistGrid pg) {
       // 160-byte rows of d = 80 spread over the banks as they are.
       constexpr int RBYTES = D * 2;
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's V reads are done
-      __builtin_amdgcn_s_barrier();
+      wg_barrier();
       char* const stage = vslot + wave * 32 * ROW;  // this wave's half of the slot
       // Offsets are made opaque per query block so that the compiler keeps
       // one register for them rather than hoisting every derived address
@@ -1001,7 +1010,7 @@ struct CalibCtx {
   template <int SLOT>
   __device__ __forceinline__ void step(int j) {
     wait_tile<Dma::IPT>(min(NBUF - 2, Nb - 1 - j));
-    __builtin_amdgcn_s_barrier();
+    wg_barrier();
     if (j + NBUF - 1 < Nb) {
       constexpr int NEXT = (SLOT + NBUF - 1) % NBUF;
       dma.issue(ring + NEXT * Shape<D>::SLOT, kbase, vbase, j + NBUF - 1, N);
