@@ -19,17 +19,22 @@
 // of tiles are issued from inline asm that waits for them itself: the
 // compiler would otherwise wait for every DMA in flight before each read (it
 // cannot tell a slot being filled from one being read), which would undo the
-// overlap.  V^T operands come from ds_read_b64_tr_b16.  The softmax reference
-// max is raised lazily (only when a block max exceeds it by more than a factor
-// 2^8 in probability), which keeps the accumulator rescale off the common path.
+// overlap.  V^T operands come from ds_read_b64_tr_b16.  At d_pad 64 both
+// kernels first walk with a fixed softmax reference (the cached row max in the
+// sparse step, key block 0's row max in the calibration) and walk a query
+// block again where a row sum leaves the float32 range; that walk, and every
+// walk at d_pad 80, raises the reference lazily (only when a block max exceeds
+// it by more than a factor 2^8 in probability), which keeps the accumulator
+// rescale off the common path.
 //
 // Sparse kernel: persistent, XCD-aware; one K slot and one V slot per
 // two-wave workgroup and at most 128 VGPRs, so that many workgroups share a
 // CU and hide each other's memory latency.  A query block's accumulator
 // starts as its cached residual.
 // Calibration kernel: QB query blocks (2 waves each) share every K/V tile; key
-// blocks are visited in ascending order and each wave adds a block either to
-// its kept accumulator or to its residual accumulator (a wave-uniform choice).
+// blocks are visited in ascending order; each wave adds every block to an
+// all-keys accumulator and its kept blocks also to a kept accumulator, and the
+// residual is their difference.
 #include "internal.h"
 
 namespace rettn {
@@ -1007,8 +1012,12 @@ struct CalibCtx {
   f32x16 oall[NT], okept[NT];
   float zall, zk;
 
+  // lazy: the reference max follows the running row max (rescaling when it
+  // rises past 2^8).  Otherwise it stays at block 0's row max and only the
+  // running max of the raw scores is kept, per lane (no exchange per block);
+  // a row sum that leaves the float32 range is caught after the walk.
   template <int SLOT>
-  __device__ __forceinline__ void step(int j) {
+  __device__ __forceinline__ void step(int j, bool lazy) {
     wait_tile<Dma::IPT>(min(NBUF - 2, Nb - 1 - j));
     wg_barrier();
     if (j + NBUF - 1 < Nb) {
@@ -1020,16 +1029,27 @@ struct CalibCtx {
     f32x16 s[2];
     if constexpr (D == 80) scores_lean<D, SLOT * Shape<D>::SLOT>(s, st, fr, min(kBlock, N - j * kBlock));
     else scores<D, SLOT * Shape<D>::SLOT>(s, st, fr, min(kBlock, N - j * kBlock));
-    bool any;
-    const float corr = update_max(st.m_ref, st.m_true, row_max(s), c, &any);
-    if (any) {
-      zall *= corr;
-      zk *= corr;
+    if (lazy) {
+      bool any;
+      const float corr = update_max(st.m_ref, st.m_true, row_max(s), c, &any);
+      if (any) {
+        zall *= corr;
+        zk *= corr;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        oall[t] *= corr;
-        okept[t] *= corr;
+        for (int t = 0; t < NT; ++t) {
+          oall[t] *= corr;
+          okept[t] *= corr;
+        }
       }
+    } else {
+      float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        m0 = fmaxf(m0, s[0][i]);
+        m1 = fmaxf(m1, s[1][i]);
+      }
+      st.m_true = fmaxf(st.m_true, fmaxf(m0, m1));
+      if (j == 0) st.m_ref = pair_max(st.m_true);
     }
     bf16x8 p[2][2];
     const float zb = probs(p, s, st.m_ref, c);  // float32 sums of the exact exponentials
@@ -1083,6 +1103,7 @@ calib_kernel(AttnArgs a, XcdGrid grid) {
     }
   }
 
+  __shared__ int redo[2 * QB];
   CalibCtx<D, NBUF, QB> cx;
   const int row = qi * kBlock + (wave & 1) * 32 + l32;
   const bool row_ok = qi < Nb && row < N;
@@ -1102,18 +1123,41 @@ calib_kernel(AttnArgs a, XcdGrid grid) {
   cx.zall = cx.zk = 0.f;
   __syncthreads();  // flags and Q in place
 
+  // d_pad 64 walks first with the reference fixed at block 0's row max.  A
+  // wave whose row sums reach 2^64 (or are not finite) walks again with the
+  // lazy maximum; the other waves keep their results and only take part in
+  // the tile loads and barriers of that walk.
+  bool lazy = D != 64;
+  for (;;) {
 #pragma unroll
-  for (int t = 0; t < NBUF - 1; ++t)
-    if (t < Nb) cx.dma.issue(ring + t * Shape<D>::SLOT, cx.kbase, cx.vbase, t, N);
-
-  for (int j = 0; j < Nb; j += NBUF) {
-    cx.template step<0>(j);
-    if (j + 1 < Nb) cx.template step<1>(j + 1);
-    if constexpr (NBUF > 2)
-      if (j + 2 < Nb) cx.template step<2>(j + 2);
+    for (int t = 0; t < NBUF - 1; ++t)
+      if (t < Nb) cx.dma.issue(ring + t * Shape<D>::SLOT, cx.kbase, cx.vbase, t, N);
+    for (int j = 0; j < Nb; j += NBUF) {
+      cx.template step<0>(j, lazy);
+      if (j + 1 < Nb) cx.template step<1>(j + 1, lazy);
+      if constexpr (NBUF > 2)
+        if (j + 2 < Nb) cx.template step<2>(j + 2, lazy);
+    }
+    if (lazy) break;
+    const bool bad = cx.active && __ballot(!(pair_sum(cx.zall) < 0x1p64f)) != 0ull;  // every lane votes
+    if (lane == 0) redo[wave] = bad;
+    wg_barrier();  // also: every wave is done with the ring before it is refilled
+    bool again = false;
+#pragma unroll
+    for (int w = 0; w < 2 * QB; ++w) again |= redo[w] != 0;
+    if (!again) break;
+    cx.active = bad;
+    if (bad) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) cx.oall[t] = cx.okept[t] = f32x16{};
+      cx.zall = cx.zk = 0.f;
+      cx.st.m_ref = cx.st.m_true = -INFINITY;
+    }
+    lazy = true;
   }
 
   // Statistics relative to the true row max m: factor e^{m_ref - m}.
+  cx.st.m_true = pair_max(cx.st.m_true);  // the fixed-reference walk keeps a per-lane max
   const float f = __builtin_amdgcn_exp2f((cx.st.m_ref - cx.st.m_true) * cx.c);
   const float zs = pair_sum(cx.zk) * f;
   const float zf = pair_sum(cx.zall) * f;

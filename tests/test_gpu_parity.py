@@ -630,6 +630,66 @@ def test_sparse_rows_beyond_the_reference_range(variant):
                 got.append(oh[b, h, rows])
     gu.assert_close(np.concatenate(got), np.concatenate(ref))
 
+def test_calibration_rows_beyond_the_first_block_range():
+    """Calibration at d_pad 64 first takes P against the row max of key block
+    0.  For six heads a key block late in the sequence is scaled by 20, so
+    many rows score it more than 64 ln 2 above block 0 and their first-walk
+    row sums pass 2^64: waves holding such rows walk again with the per-block
+    maximum.  That block is in none of the six heads' lists, so Z_sparse of
+    such rows can lie far below float32's normal range (their kept mass can be
+    e^-100 of the row's); it is compared where the oracle's is at least 1e-30
+    and must be tiny elsewhere.  Every third
+    32-row group of those heads has q = 0 (all scores 0, never out of range),
+    so workgroups mix waves that walk again with waves that keep their first
+    walk.  Output and statistics of sampled query blocks are compared with the
+    oracle, on the six heads and on two heads without the scaled block."""
+    say("calibration rows beyond the first block's range")
+    B, H, d, keep = 1, 8, 64, 5
+    N = 64 * 150 + 41
+    nb = (N + 63) // 64
+    hot = nb - 4
+    q, k, v = synth.random_qkv(B, H, N, d, d, seed=321, scale=1.0, dtype="bf16", device=gu.DEV)
+    k[:, :6, hot * 64:(hot + 1) * 64] *= 20.0
+    calm = (np.arange(N) // 32) % 3 == 0
+    q[:, :6, torch.as_tensor(calm, device=q.device)] = 0
+    # the scaled block is masked for the six heads: R carries it (a kept block
+    # that dominates would leave R = all - kept to float32 cancellation)
+    g = np.random.default_rng(5)
+    others = np.delete(np.arange(nb), hot)
+    idx = np.sort(np.stack([[[g.choice(others if h < 6 else nb, keep, replace=False) for _ in range(nb)]
+                             for h in range(H)] for _ in range(B)]), axis=-1).astype(np.int32)
+    sh = rettn.shape(B, H, N, d, d, keep, "bf16")
+    cache = rettn.StatsCache(sh, 1)
+    o = gu.calibrate(sh, q, k, v, torch.as_tensor(idx).to(gu.DEV), cache)
+    torch.cuda.synchronize()
+    t = cache.tensors(0)
+    qh, kh, vh, oh = gu.host(q), gu.host(k), gu.host(v), gu.host(o)
+    # the data does leave the first walk's range: a row sum of exponentials
+    # against block 0's max passes 2^64 once a score exceeds that max by
+    # 64 ln 2 (scores scaled by 1/sqrt(d))
+    s0 = qh[0, 0, 32:64] @ kh[0, 0, :64].T / np.sqrt(d)
+    s_hot = qh[0, 0, 32:64] @ kh[0, 0, hot * 64:(hot + 1) * 64].T / np.sqrt(d)
+    assert (s_hot.max(axis=1) - s0.max(axis=1)).max() > 64 * np.log(2.0)
+    w = gu.Worst("calibration beyond the first block's range")
+    tiny = 0
+    for h in range(H):
+        for i in sorted({0, 1, 2, 3, nb // 2, hot, nb - 1} | set(g.choice(nb, 3, replace=False).tolist())):
+            rows = gu.block_rows(N, i)
+            st = oracle.calibrate_rows(qh[0, h], kh[0, h], vh[0, h], rows, idx[0, h, i], N, d)
+            w.add(oh[0, h, rows], st["o"], (h, i))
+            m = gu.host(t["m"][0, h, rows])
+            assert np.abs(m - st["m"]).max() <= 1e-4 * max(1.0, np.abs(st["m"]).max()), ("m", h, i)
+            assert np.abs(gu.host(t["z_full"][0, h, rows]) / st["z_full"] - 1).max() <= 1e-4, ("z_full", h, i)
+            zs, ok = gu.host(t["z_sparse"][0, h, rows]), st["z_sparse"] >= 1e-30
+            assert np.abs(zs[ok] / st["z_sparse"][ok] - 1).max(initial=0.0) <= 1e-4, ("z_sparse", h, i)
+            assert np.all(zs[~ok] <= 1e-29), ("z_sparse tiny", h, i)
+            tiny += int((~ok).sum())
+            r = gu.r_rows(t["R"], sh, 0, h, rows)
+            assert np.abs(r - st["r"]).sum() <= 3e-3 * max(1e-30, np.abs(st["r"]).sum()), ("R", h, i)
+    w.check()
+    print(f"[info] {tiny} rows with Z_sparse below 1e-30", flush=True)
+    cache.close()
+
 
 @pytest.mark.parametrize("dtype,D,d", [("bf16", 64, 64), ("bf16", 80, 72), ("f32", 64, 64)])
 def test_repeated_list_entries_count_once(dtype, D, d):
