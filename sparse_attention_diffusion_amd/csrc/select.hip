@@ -216,8 +216,8 @@ __device__ __forceinline__ void wave_sync() {
 constexpr int kMaxRounds = 32;  // above this many non-forced winners: bitonic sort
 constexpr int kMaxSelLds = 64 << 10;  // dynamic LDS of one selecting workgroup at most
 
-// Query blocks per wave: 4 (2 above 512 key blocks, where the per-lane
-// scores take more registers), so that many waves share each SIMD.
+// Query blocks per wave, at most: 4 (2 above 512 key blocks, where the
+// per-lane scores take more registers), so that many waves share each SIMD.
 template <int CH>
 constexpr int query_group() { return CH <= 8 ? 4 : 2; }
 
@@ -261,7 +261,8 @@ __device__ __forceinline__ void emit(const unsigned char* flags, int Nb, int32_t
 // The selecting kernel: pools its query blocks straight from q, scores them
 // against the K means and takes each one's kept list.  One workgroup of
 // W waves (4, or 2 where four would need more than 64 KB of LDS) per
-// (bh, W * QG query blocks); wave w owns QG consecutive query blocks.
+// (bh, W * QG query blocks); wave w owns QG consecutive query blocks (QG is
+// chosen per call, up to query_group<CH>()).
 //   1. pooling: the rows of each of the wave's query blocks are read as
 //      16-byte chunks, all at once, summed in float32 per row group and
 //      reduced through the wave's LDS (then multiplied by 1/rows);
@@ -276,9 +277,8 @@ __device__ __forceinline__ void emit(const unsigned char* flags, int Nb, int32_t
 // Only the staging of the K means synchronises the workgroup; everything
 // else is wave-local, so waves with fewer (or no) query blocks never hold
 // the others at a barrier.
-template <typename T, int D, int CH, int W>
+template <typename T, int D, int CH, int W, int QG>
 __global__ void __launch_bounds__(64 * W) select_kernel(SelectArgs a, XcdGrid grid, SelectLds lay) {
-  constexpr int QG = query_group<CH>();
   constexpr int E = Chunk<T>::E, CPR = D / E, RPI = 64 / CPR, PASSES = (kBlock + RPI - 1) / RPI;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int KCS = D + 4;  // floats per key block row of the staged chunk
@@ -512,21 +512,36 @@ __global__ void __launch_bounds__(64 * W) select_kernel(SelectArgs a, XcdGrid gr
   }
 }
 
-template <typename T, int D, int CH>
-void launch_select_ch(const SelectArgs& a, hipStream_t s) {
-  constexpr int QG = query_group<CH>();
+template <typename T, int D, int CH, int QG>
+void launch_select_qg(const SelectArgs& a, bool bitonic, hipStream_t s) {
   constexpr int RPI = 64 / (D / Chunk<T>::E);
-  int n_forced = 0;
-  for (int w = 0; w < kMaxBlocks / 32; ++w) n_forced += __builtin_popcount(a.forced[w]);
-  const bool bitonic = a.keep - n_forced > kMaxRounds;
   const SelectLds l4 = select_lds(4, QG, D, RPI, a.Nb, bitonic);
   if (l4.bytes <= kMaxSelLds) {
     XcdGrid sg = make_xcd_grid((uint32_t)a.BH * (uint32_t)((a.Nb + 4 * QG - 1) / (4 * QG)));
-    hipLaunchKernelGGL((select_kernel<T, D, CH, 4>), dim3(sg.grid()), dim3(256), l4.bytes, s, a, sg, l4);
+    hipLaunchKernelGGL((select_kernel<T, D, CH, 4, QG>), dim3(sg.grid()), dim3(256), l4.bytes, s, a, sg, l4);
   } else {
     const SelectLds l2 = select_lds(2, QG, D, RPI, a.Nb, bitonic);
     XcdGrid sg = make_xcd_grid((uint32_t)a.BH * (uint32_t)((a.Nb + 2 * QG - 1) / (2 * QG)));
-    hipLaunchKernelGGL((select_kernel<T, D, CH, 2>), dim3(sg.grid()), dim3(128), l2.bytes, s, a, sg, l2);
+    hipLaunchKernelGGL((select_kernel<T, D, CH, 2, QG>), dim3(sg.grid()), dim3(128), l2.bytes, s, a, sg, l2);
+  }
+}
+
+// Query blocks per wave: the most (each wave then reads the K means once for
+// more query blocks) that still give at least 1536 four-wave workgroups;
+// smaller calls are latency-bound and run faster as more, shorter workgroups
+// (measured: 4 best at B*H*Nb = 96*278, 2 at 60*278, 1 at 32*64).
+template <typename T, int D, int CH>
+void launch_select_ch(const SelectArgs& a, hipStream_t s) {
+  int n_forced = 0;
+  for (int w = 0; w < kMaxBlocks / 32; ++w) n_forced += __builtin_popcount(a.forced[w]);
+  const bool bitonic = a.keep - n_forced > kMaxRounds;
+  if constexpr (query_group<CH>() == 4) {
+    auto wgs = [&](int qg) { return (uint32_t)a.BH * (uint32_t)((a.Nb + 4 * qg - 1) / (4 * qg)); };
+    if (wgs(4) >= 1536u) launch_select_qg<T, D, CH, 4>(a, bitonic, s);
+    else if (wgs(2) >= 1536u) launch_select_qg<T, D, CH, 2>(a, bitonic, s);
+    else launch_select_qg<T, D, CH, 1>(a, bitonic, s);
+  } else {
+    launch_select_qg<T, D, CH, query_group<CH>()>(a, bitonic, s);
   }
 }
 
