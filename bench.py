@@ -43,6 +43,9 @@ def parse():
                    help="skip the cogvideox5b schedule over all 42 layers (caches resident)")
     p.add_argument("--cpu-heads", type=int, default=2)
     p.add_argument("--cpu-budget-s", type=float, default=10.0)
+    p.add_argument("--oracle-timing", action="store_true",
+                   help="time the oracle (float32, host cores) over whole layers at every configuration: one "
+                        "sparse step and one calibration each (cogvideox5b: the calibration of layers 0 and 41)")
     p.add_argument("--traffic-probe", action="store_true",
                    help="first run a plain 512 MiB device copy (reference for HBM byte counters)")
     p.add_argument("--no-components", action="store_true",
@@ -138,6 +141,51 @@ def cpu_baseline(cfg, heads, budget_s, dtype="f32"):
                       "s_full_layer_est": t_cal * (bh / heads)},
         "cpu_model": _cpu_model(),
     }
+
+
+def oracle_full_timing(name, dtype="f32"):
+    """The oracle timed over a whole layer of configuration ``name`` on this
+    host's cores: the calibration on step 0 and one sparse reshape step (step
+    1) with its lists, every head of the layer.  For cogvideox5b the
+    calibration is timed on layers 0 and 41 (seeds 1000 + layer), each a whole
+    layer; its sparse step on layer 0.  No GPU is used."""
+    import numpy as np
+    import oracle
+    from sparse_attention_diffusion_amd import configs, synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    cfg = configs.CONFIGS[name]
+    N, d, keep = cfg["N"], cfg["d"], cfg["keep"]
+    forced = configs.forced_blocks(cfg)
+    npdt = np.float32 if dtype == "f32" else np.float64
+    host = lambda t: synth.store(t, cfg["dtype"]).float().numpy().astype(npdt)
+    layers = [0, cfg["layers"] - 1] if cfg["layers"] > 1 else [0]
+    cal_s, sparse_s, flops = [], None, 0
+    for layer in layers:
+        it = synth.StepInputs(cfg, seed=1000 + layer if cfg["layers"] > 1 else 0, device="cpu")
+        q0, k0, v0 = (host(t) for t in it.next())
+        idx = oracle.select_blocks(q0, k0, N, d, keep, forced, dtype=npdt)
+        t0 = time.perf_counter()
+        st = oracle.calibrate(q0, k0, v0, idx, N, d, dtype=npdt)
+        cal_s.append(time.perf_counter() - t0)
+        del q0, k0, v0
+        if sparse_s is None:
+            q, k, v = (host(t) for t in it.next())
+            t0 = time.perf_counter()
+            oracle.sparse_reshape(q, k, v, idx, st, N, d, dtype=npdt)
+            sparse_s = time.perf_counter() - t0
+            flops = oracle.kept_flops(idx, N, d)
+            del q, k, v
+        del st, it
+    dense = 4 * d * N * N * cfg["B"] * cfg["H"]
+    return {"study": "oracle over whole layers", "config": name, "dtype": dtype, "cores": threads,
+            "cpu_model": _cpu_model(), "heads": cfg["B"] * cfg["H"],
+            "sparse_step_s": round(sparse_s, 3), "sparse_kept_tflops": flops / sparse_s / 1e12,
+            "calibrate_layers": layers, "calibrate_s": [round(t, 2) for t in cal_s],
+            "calibrate_dense_tflops": dense / float(np.mean(cal_s)) / 1e12}
 
 
 def hilbert_reorder(cfg, sh, dev):
@@ -448,6 +496,10 @@ def main():
     import torch
     from sparse_attention_diffusion_amd import configs, rettn, synth
 
+    if args.oracle_timing:
+        for name in configs.ORDER:
+            print(json.dumps(oracle_full_timing(name, args.cpu_dtype)), flush=True)
+        return
     if args.fidelity:
         print(json.dumps(fidelity(dict(configs.CONFIGS[args.config], name=args.config), args.period, args.order)),
               flush=True)

@@ -33,6 +33,14 @@ def test_kept_flops_and_bytes_by_hand():
     assert bench.sparse_call_bytes(idx, N, D, 2) == want
 
 
+def test_oracle_full_timing_tiny():
+    bench = _bench()
+    r = bench.oracle_full_timing("tiny")
+    assert r["config"] == "tiny" and r["dtype"] == "f32" and r["heads"] == 2
+    assert r["calibrate_layers"] == [0] and len(r["calibrate_s"]) == 1
+    assert r["sparse_step_s"] > 0 and r["sparse_kept_tflops"] > 0 and r["calibrate_dense_tflops"] > 0
+
+
 def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
