@@ -171,6 +171,7 @@ def oracle_full_timing(name, dtype="f32"):
         t0 = time.perf_counter()
         st = oracle.calibrate(q0, k0, v0, idx, N, d, dtype=npdt)
         cal_s.append(time.perf_counter() - t0)
+        print(f"oracle timing {name}: layer {layer} calibration {cal_s[-1]:.1f} s", file=sys.stderr, flush=True)
         del q0, k0, v0
         if sparse_s is None:
             q, k, v = (host(t) for t in it.next())
