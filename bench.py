@@ -307,6 +307,7 @@ def components(cfg, reps=20, flush_mb=512, order="raster"):
         "select_ms": round(t_sel, 4), "select_hbm_gbs": round(sel_bytes / (t_sel * 1e-3) / 1e9, 1),
         "calibrate_ms": round(t_cal, 4), "calibrate_tflops": round(dense / (t_cal * 1e-3) / 1e12, 1),
         "calibrate_mfma_frac": round(dense / (t_cal * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "calibrate_stats_residual_write_gbs": round((sh.B * sh.H * N * (D * 4 + 12)) / (t_cal * 1e-3) / 1e9, 1),
         "sparse_warm_ms": round(t_warm, 5), "sparse_warm_p10_p50_p90": pw,
         "sparse_cold_ms": round(t_cold, 5), "sparse_cold_p10_p50_p90": pc,
         "sparse_kept_tflops_warm": round(flop / (t_warm * 1e-3) / 1e12, 1),
