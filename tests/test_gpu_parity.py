@@ -342,6 +342,15 @@ def test_parity_cogvideox2b_sampled_r2():
     run_sampled_parity(cfg, heads=[(0, 7), (1, 23)], n_steps=4, check_steps=(1, 3), variant="r2")
 
 
+def test_parity_cogvideox2b_sampled_r2_bf16_residual():
+    """The d_pad 64 sparse kernel with both options at once (R2 epilogue,
+    residual cached in bf16), against the exact oracle and against the oracle
+    fed the rounded residual."""
+    say("parity cogvideox2b sampled r2 bf16 residual")
+    cfg = configs.CONFIGS["cogvideox2b"]
+    run_sampled_parity(cfg, heads=[(0, 11), (1, 5)], n_steps=3, check_steps=(2,), residual="bf16", variant="r2")
+
+
 def test_r1_through_ex_is_the_default_entry_point():
     """rt_sparse_attn_reshape_ex with RT_RESHAPE_R1 is bit-identical to
     rt_sparse_attn_reshape; R2 on the calibration inputs gives dense attention
@@ -567,8 +576,8 @@ def test_sparse_many_blocks_per_workgroup(keep, variant):
     gu.assert_close(np.concatenate(got), np.concatenate(ref))
 
 
-@pytest.mark.parametrize("variant", ["r1", "r2"])
-def test_sparse_rows_beyond_the_reference_range(variant):
+@pytest.mark.parametrize("variant,residual", [("r1", "f32"), ("r2", "f32"), ("r1", "bf16"), ("r2", "bf16")])
+def test_sparse_rows_beyond_the_reference_range(variant, residual):
     """Rows whose scores rise far above the reference the first walk takes P
     against: the cached row max (R1; set 200 below the scores for one head) or
     the first listed tile's row max (R2; every list of six heads ends with a
@@ -576,8 +585,9 @@ def test_sparse_rows_beyond_the_reference_range(variant):
     than float32 exponentials hold).  Those blocks overflow on the first walk
     and are walked again with the per-tile maximum; with several query blocks
     per workgroup the blocks after a redone one must come out right too.  All
-    sampled blocks are compared with the oracle."""
-    say("sparse rows beyond the reference range", variant)
+    sampled blocks are compared with the oracle (fed the stored residual:
+    rounded to bf16 where the cache holds it in bf16)."""
+    say("sparse rows beyond the reference range", variant, residual)
     B, H, d, keep = 2, 16, 64, 5
     N = 64 * 170 + 23
     nb = (N + 63) // 64
@@ -602,7 +612,7 @@ def test_sparse_rows_beyond_the_reference_range(variant):
     z_f = z_s * g.uniform(1.0, 4.0, (B, H, N))
     r_c = g.normal(0.0, 0.5, (B, H, N, d))
     sh = rettn.shape(B, H, N, d, d, keep, "bf16")
-    cache = rettn.StatsCache(sh, 1)
+    cache = rettn.StatsCache(sh, 1, residual=residual)
     t = cache.tensors(0)
     t["m"].copy_(torch.as_tensor(m_c, dtype=torch.float32))
     t["z_full"].copy_(torch.as_tensor(z_f, dtype=torch.float32))
@@ -613,6 +623,8 @@ def test_sparse_rows_beyond_the_reference_range(variant):
     o = gu.sparse(sh, q, k, v, cache, variant=variant)
     torch.cuda.synchronize()
     m32, zf32, zs32, r32 = (x.astype(np.float32) for x in (m_c, z_f, z_s, r_c))
+    if residual == "bf16":
+        r32 = bf16_round(r_c)
     qh, kh, vh, oh = gu.host(q), gu.host(k), gu.host(v), gu.host(o)
     # the data does leave the range: scores of the hot block exceed those of a
     # list's first block by more than 88 (e^88 is near the float32 limit)
@@ -630,7 +642,8 @@ def test_sparse_rows_beyond_the_reference_range(variant):
                 got.append(oh[b, h, rows])
     gu.assert_close(np.concatenate(got), np.concatenate(ref))
 
-def test_calibration_rows_beyond_the_first_block_range():
+@pytest.mark.parametrize("residual", ["f32", "bf16"])
+def test_calibration_rows_beyond_the_first_block_range(residual):
     """Calibration at d_pad 64 first takes P against the row max of key block
     0.  For six heads a key block late in the sequence is scaled by 20, so
     many rows score it more than 64 ln 2 above block 0 and their first-walk
@@ -642,8 +655,9 @@ def test_calibration_rows_beyond_the_first_block_range():
     32-row group of those heads has q = 0 (all scores 0, never out of range),
     so workgroups mix waves that walk again with waves that keep their first
     walk.  Output and statistics of sampled query blocks are compared with the
-    oracle, on the six heads and on two heads without the scaled block."""
-    say("calibration rows beyond the first block's range")
+    oracle, on the six heads and on two heads without the scaled block; with
+    the residual cached in bf16 as well (R within the same L1 bound)."""
+    say("calibration rows beyond the first block's range", residual)
     B, H, d, keep = 1, 8, 64, 5
     N = 64 * 150 + 41
     nb = (N + 63) // 64
@@ -659,7 +673,7 @@ def test_calibration_rows_beyond_the_first_block_range():
     idx = np.sort(np.stack([[[g.choice(others if h < 6 else nb, keep, replace=False) for _ in range(nb)]
                              for h in range(H)] for _ in range(B)]), axis=-1).astype(np.int32)
     sh = rettn.shape(B, H, N, d, d, keep, "bf16")
-    cache = rettn.StatsCache(sh, 1)
+    cache = rettn.StatsCache(sh, 1, residual=residual)
     o = gu.calibrate(sh, q, k, v, torch.as_tensor(idx).to(gu.DEV), cache)
     torch.cuda.synchronize()
     t = cache.tensors(0)
