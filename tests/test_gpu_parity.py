@@ -67,6 +67,38 @@ def test_selector_exact_on_exact_scores(N, keep, forced, dtype):
     assert np.array_equal(idx.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("B,H,N,D,keep,forced,dtype", [
+    (1, 2, 64 * 100, 80, 9, [3], "bf16"),                   # d_pad 80, two 64-block chunks, rounds
+    (1, 2, 64 * 278 - 16, 80, 40, [0, 1, 2, 3], "bf16"),    # d_pad 80, five chunks, bitonic sort
+    (1, 2, 64 * 600 + 17, 80, 40, [], "bf16"),              # d_pad 80 above 512 blocks, bitonic: two-wave launch
+    (1, 2, 64 * 600 + 17, 80, 9, [0], "bf16"),              # d_pad 80 above 512 blocks, rounds
+    (1, 2, 64 * 300, 64, 20, [], "f32"),                    # float32 inputs, five chunks
+    (1, 2, 64 * 700 + 5, 80, 40, [1], "f32"),               # float32, d_pad 80, sixteen chunks, bitonic
+    (1, 48, 64 * 278 - 16, 64, 9, [0, 1, 2, 3], "bf16"),    # two query blocks per wave
+    (1, 96, 64 * 278 - 16, 64, 9, [0, 1, 2, 3], "bf16"),    # four query blocks per wave
+    (1, 96, 64 * 278 - 16, 64, 40, [0, 1, 2, 3], "bf16"),   # four per wave, bitonic sort
+])
+def test_selector_instantiations_exact(B, H, N, D, keep, forced, dtype):
+    """Bit-exact lists and scores, on exactly representable inputs, for the
+    selector instantiations the workload shapes above do not reach: d_pad 80
+    with several 64-block chunks (and the two-wave launch that the bitonic
+    path needs above 512 key blocks), float32 inputs with several chunks, and
+    two and four query blocks per wave (chosen by the workgroup count).  The
+    true head dim is 64 (scale 1/8, exact); channels 64.. are zero."""
+    say("selector instantiation", B, H, N, D, keep, forced, dtype)
+    d = 64
+    q, k = block_constant_inputs(B, H, N, D, seed=N + H, dtype=dtype)
+    q[..., d:] = 0
+    k[..., d:] = 0
+    sh = rettn.shape(B, H, N, d, D, keep, dtype)
+    idx, scores = gu.select(sh, q.to(gu.DEV), k.to(gu.DEV), forced)
+    hq, hk = gu.host(q), gu.host(k)
+    ref_scores = oracle.pooled_scores(hq, hk, N, d)
+    assert np.array_equal(scores.cpu().numpy().astype(np.float64), ref_scores)
+    ref = oracle.select_blocks(hq, hk, N, d, keep, forced, scores=ref_scores)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("name", ["tiny", "pixart512", "pixart1024", "cogvideox2b"])
 def test_selector_on_workload(name):
     say("selector workload", name)
